@@ -1,0 +1,226 @@
+"""Benchmark of the shared-expert SwiGLU MLP on one MI355X.
+
+Default workload: Kimi-K3 shared expert, replicated decode, M = 16 tokens,
+H = 7168, I = 6144, bf16 weights with fp32 accumulation and bf16 output, 8 distinct
+weight copies cycled per call (2.1 GB, beyond the 256 MB Infinity Cache).  One step
+is one layer forward: the gate_up + SiLU-and-mul kernel followed by the down kernel,
+on inputs already resident in HBM.
+
+Prints one JSON line (rank 0).  ``value`` is the achieved algorithmic HBM bandwidth
+(weights + x + out bytes per layer / time per layer).  ``roofline`` reports the
+dominant kernel (gate_up) timed with HIP events on its stream inside the timed
+region.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.  ``--sweep`` adds one line per (layout, M) of the M sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from moe_shared_expert_amd import binding, roofline  # noqa: E402
+
+METRIC = "µs/layer & achieved HBM GB/s (% of 8 TB/s) for shared-expert MLP at M=1–8192"
+H, I = synth.HIDDEN, synth.INTERMEDIATE
+
+WORKLOADS = {
+    # name: (M, I_r, partial_fp32, copies, config id, description)
+    "decode_rep_m16": (16, I, False, 8, 2,
+                       "Kimi-K3 shared expert, replicated decode, M=16, H=7168, I=6144, bf16 out, "
+                       "8 weight copies cycled"),
+    "tp8_shard_m128": (128, 768, True, 16, 3,
+                       "TP8 per-rank shard, M=128, H=7168, I_r=768, fp32 partial out, 16 copies cycled"),
+    "prefill_rep_m8192": (8192, I, False, 2, 5,
+                          "replicated prefill, M=8192, H=7168, I=6144, bf16 out, 2 copies cycled"),
+}
+
+
+def _ev():
+    return torch.cuda.Event(enable_timing=True)
+
+
+def make_inputs(M, I_r, copies, cfg, dev):
+    x = synth.activations(M, H, config=cfg).to(dev)
+    ws = []
+    for c in range(copies):
+        wgu, wd = synth.layer_weights(H, I_r, config=cfg, copy=c, fan_in_down=I)
+        ws.append((wgu.to(dev), wd.to(dev)))
+    return x, ws
+
+
+def run_workload(name, steps, warmup, dev, per_kernel=True):
+    M, I_r, partial, copies, cfg, desc = WORKLOADS[name]
+    x, weights = make_inputs(M, I_r, copies, cfg, dev)
+    odt = torch.float32 if partial else torch.bfloat16
+    out = torch.empty(M, H, dtype=odt, device=dev)
+    wsb = binding.shared_mlp_workspace_bytes(M, H, I_r, binding.SMLP_BF16)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = binding.shared_mlp_plan(M, H, I_r, binding.SMLP_BF16, partial)
+
+    def step(i, evs=None):
+        g, d = weights[i % copies]
+        if evs is None:
+            binding.shared_mlp_forward(x, g, d, out, partial, ws, stream)
+        else:
+            evs[0].record(stream)
+            binding.shared_mlp_gate_up_act(x, g, ws, partial, stream)
+            evs[1].record(stream)
+            binding.shared_mlp_down(d, out, ws, partial, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Timed region: K steps; each step is the two stage calls with an event pair around
+    # the dominant (gate_up) kernel(s).
+    kev = [(_ev(), _ev()) for _ in range(steps)] if per_kernel else None
+    t0, t1 = _ev(), _ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(i, kev[i] if per_kernel else None)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    gu_us = None
+    if per_kernel:
+        gu_us = 1e3 * sum(a.elapsed_time(b) for a, b in kev) / steps
+    out_elem = 4 if partial else 2
+    alg = roofline.algorithmic_bytes(M, H, I_r, 2, out_elem)
+    fl = roofline.flops(M, H, I_r)
+    res = {
+        "name": name, "desc": desc, "M": M, "I_r": I_r, "partial": partial, "copies": copies,
+        "ms_per_step": ms, "us_per_layer": ms * 1e3, "alg_bytes": alg, "flops": fl,
+        "gbs": alg / (ms * 1e-3) / 1e9, "tflops": fl / (ms * 1e-3) / 1e12, "plan": plan,
+    }
+    if gu_us is not None:
+        h_bytes = M * I_r * (4 if plan["h_dtype"] == binding.SMLP_FP32 else 2)
+        gu_alg = roofline.gate_up_bytes(H, I_r) + M * H * 2 + h_bytes
+        res["gate_up_us"] = gu_us
+        res["gate_up_alg_bytes"] = gu_alg
+        res["gate_up_gbs"] = gu_alg / (gu_us * 1e-6) / 1e9
+    return res
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """The fp64 oracle on host cores, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    M, I_r, partial, copies, cfg, desc = WORKLOADS[name]
+    x = synth.to_f64(synth.activations(M, H, config=cfg))
+    layers = []
+    for c in range(2):
+        wgu, wd = synth.layer_weights(H, I_r, config=cfg, copy=c, fan_in_down=I)
+        layers.append((synth.to_f64(wgu), synth.to_f64(wd)))
+    oracle.swiglu_mlp(x[:1], *layers[0])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.swiglu_mlp(x, *layers[n % 2])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (el > 0 and n >= 1 and el / n * (n + 1) > 3 * budget_s):
+            break
+    per_layer = el / n
+    alg = roofline.algorithmic_bytes(M, H, I_r, 2, 4 if partial else 2)
+    return {"value": alg / per_layer / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} layer forwards of the {desc} workload (2 weight copies cycled), "
+                      f"numpy fp64 oracle, {per_layer * 1e3:.1f} ms per layer",
+            "seconds_per_layer": per_layer, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode_rep_m16", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also print the M sweep lines")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path "
+                                   "(all-gather / reduce-scatter over RCCL) is not built"}))
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    binding.lib()
+    r = run_workload(args.workload, args.steps, args.warmup, dev)
+    line = {
+        "metric": METRIC, "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": r["desc"], "M": r["M"], "H": H, "I": r["I_r"],
+                   "layout": "tp-shard" if r["partial"] else "replicated",
+                   "out": "fp32 partial" if r["partial"] else "bf16",
+                   "weight_copies": r["copies"], "path": r["plan"]["path_name"]},
+        "us_per_layer": round(r["us_per_layer"], 3),
+        "hbm_frac": round(r["gbs"] / roofline.HBM_PEAK_GBS, 4),
+        "tflops": round(r["tflops"], 2),
+        "roofline": {"bound": "hbm", "kernel": "gate_up + SiLU-and-mul",
+                     "achieved": round(r["gate_up_gbs"], 1), "peak": roofline.HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["gate_up_gbs"] / roofline.HBM_PEAK_GBS, 4),
+                     "kernel_us": round(r["gate_up_us"], 3),
+                     "bytes_per_launch": r["gate_up_alg_bytes"], "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+    if args.sweep:
+        sweep(dev)
+
+
+def sweep(dev):
+    """M sweep {1..8192} for the replicated layer and the TP8 shard (8 / 16 copies cycled)."""
+    Ms = [1, 8, 32, 128, 512, 2048, 8192]
+    for layout, I_r, partial, copies in (("replicated", I, False, 8), ("tp8", 768, True, 16)):
+        weights = []
+        for c in range(copies):
+            wgu, wd = synth.layer_weights(H, I_r, config=6, copy=c, fan_in_down=I)
+            weights.append((wgu.to(dev), wd.to(dev)))
+        for M in Ms:
+            x = synth.activations(M, H, config=6, copy=M).to(dev)
+            out = torch.empty(M, H, dtype=torch.float32 if partial else torch.bfloat16, device=dev)
+            ws = torch.empty(max(binding.shared_mlp_workspace_bytes(M, H, I_r, 0), 256),
+                             dtype=torch.uint8, device=dev)
+            steps = 200 if M <= 512 else 20
+            for i in range(5):
+                g, d = weights[i % copies]
+                binding.shared_mlp_forward(x, g, d, out, partial, ws)
+            torch.cuda.synchronize()
+            t0, t1 = _ev(), _ev()
+            t0.record()
+            for i in range(steps):
+                g, d = weights[i % copies]
+                binding.shared_mlp_forward(x, g, d, out, partial, ws)
+            t1.record()
+            torch.cuda.synchronize()
+            us = t0.elapsed_time(t1) * 1e3 / steps
+            alg = roofline.algorithmic_bytes(M, H, I_r, 2, 4 if partial else 2)
+            fl = roofline.flops(M, H, I_r)
+            print(json.dumps({"sweep": layout, "M": M, "I_r": I_r, "us_per_layer": round(us, 2),
+                              "gbs": round(alg / us / 1e3, 1),
+                              "hbm_frac": round(alg / us / 1e3 / roofline.HBM_PEAK_GBS, 4),
+                              "tflops": round(fl / us / 1e6, 1),
+                              "mfma_frac": round(fl / us / 1e6 / roofline.BF16_MFMA_PEAK_TFLOPS, 4),
+                              "path": binding.shared_mlp_plan(M, H, I_r, 0, partial)["path_name"]}),
+                  flush=True)
+        del weights
+
+
+if __name__ == "__main__":
+    main()

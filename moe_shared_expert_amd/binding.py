@@ -1,0 +1,206 @@
+"""ctypes binding of libsmlp.so: argument marshalling only.
+
+torch supplies device memory (tensors) and the current HIP stream; every step of
+the computation runs in the library's HIP kernels.  The library must be built
+(``python -m moe_shared_expert_amd.build``); if it is missing, loading fails with
+an error -- there is no fallback implementation.
+
+torch is imported before the library is loaded so that the library binds to the
+HIP runtime torch already loaded (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+SMLP_BF16, SMLP_FP32 = 0, 1
+PATH_NAMES = {0: "none", 1: "fp32", 2: "small_m", 3: "large_m"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmlp.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_int = ctypes.c_int
+
+
+class SmlpError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("path", _int), ("h_dtype", _int), ("h_offset", _sz), ("workspace_bytes", _sz),
+                ("gate_up_ksplit", _int), ("down_ksplit", _int), ("gate_up_blocks", _int),
+                ("down_blocks", _int), ("kernels", _int)]
+
+
+EXPORTS = {
+    "shared_mlp_status_string": (ctypes.c_char_p, [_int]),
+    "shared_mlp_last_error": (ctypes.c_char_p, []),
+    "shared_mlp_plan": (_int, [_i64, _i64, _i64, _int, _int, ctypes.POINTER(_Plan)]),
+    "shared_mlp_workspace_bytes": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
+    "shared_mlp_forward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "shared_mlp_gate_up_act": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "shared_mlp_down": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "shared_mlp_set_large_m_threshold": (_i64, [_i64]),
+    "shared_mlp_shard_eligible": (_int, [_int, _int, _int, _int, _i64, _i64]),
+    "shared_mlp_slice_rank": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "shared_mlp_rms_rescale": (_int, [_vp, _vp, _i64, _i64, _vp]),
+}
+
+
+def lib():
+    """Load libsmlp.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m moe_shared_expert_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise SmlpError(status, L.shared_mlp_status_string(status).decode(),
+                        L.shared_mlp_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SMLP_BF16
+    if t.dtype == torch.float32:
+        return SMLP_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def shared_mlp_plan(M: int, H: int, I: int, dtype: int = SMLP_BF16, partial_fp32: bool = False) -> dict:
+    p = _Plan()
+    _check(lib().shared_mlp_plan(M, H, I, dtype, int(bool(partial_fp32)), ctypes.byref(p)))
+    d = {k: getattr(p, k) for k, _ in _Plan._fields_}
+    d["path_name"] = PATH_NAMES.get(d["path"], "?")
+    return d
+
+
+def shared_mlp_workspace_bytes(M: int, H: int, I: int, dtype: int = SMLP_BF16) -> int:
+    b = _sz()
+    _check(lib().shared_mlp_workspace_bytes(M, H, I, dtype, ctypes.byref(b)))
+    return b.value
+
+
+def _shapes(x, w_gate_up, w_down, out):
+    M, H = x.shape
+    two_i, H2 = w_gate_up.shape
+    if H2 != H or two_i % 2:
+        raise ValueError(f"w_gate_up {tuple(w_gate_up.shape)} does not match x {tuple(x.shape)}")
+    I = two_i // 2
+    if w_down is not None and tuple(w_down.shape) != (H, I):
+        raise ValueError(f"w_down {tuple(w_down.shape)} != ({H}, {I})")
+    if out is not None and tuple(out.shape) != (M, H):
+        raise ValueError(f"out {tuple(out.shape)} != ({M}, {H})")
+    return M, H, I
+
+
+def _workspace(workspace, M, H, I, dtype, device):
+    need = shared_mlp_workspace_bytes(M, H, I, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def shared_mlp_forward(x, w_gate_up, w_down, out, partial_fp32=False, workspace=None, stream=None):
+    """out = down(SiLU(x Wg^T) * (x Wu^T)); out is bf16, or fp32 for partial_fp32 / fp32 inputs."""
+    M, H, I = _shapes(x, w_gate_up, w_down, out)
+    dt = _dtype_code(x)
+    workspace = _workspace(workspace, M, H, I, dt, x.device)
+    _check(lib().shared_mlp_forward(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), M, H, I, dt,
+                                    int(bool(partial_fp32)), _ptr(workspace), workspace.numel(),
+                                    _stream(stream, x.device)))
+    return out
+
+
+def shared_mlp_gate_up_act(x, w_gate_up, workspace, partial_fp32=False, stream=None):
+    M, H, I = _shapes(x, w_gate_up, None, None)
+    dt = _dtype_code(x)
+    _check(lib().shared_mlp_gate_up_act(_ptr(x), _ptr(w_gate_up), M, H, I, dt, int(bool(partial_fp32)),
+                                        _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
+
+
+def shared_mlp_down(w_down, out, workspace, partial_fp32=False, stream=None):
+    H, I = w_down.shape
+    M = out.shape[0]
+    dt = _dtype_code(w_down)
+    _check(lib().shared_mlp_down(_ptr(w_down), _ptr(out), M, H, I, dt, int(bool(partial_fp32)),
+                                 _ptr(workspace), workspace.numel(), _stream(stream, w_down.device)))
+
+
+def read_h(workspace, M: int, I: int, H: int, dtype: int = SMLP_BF16, partial_fp32=False):
+    """View of the intermediate h [M, I] inside a workspace (after shared_mlp_gate_up_act)."""
+    p = shared_mlp_plan(M, H, I, dtype, partial_fp32)
+    tdt = torch.float32 if p["h_dtype"] == SMLP_FP32 else torch.bfloat16
+    nbytes = M * I * (4 if tdt == torch.float32 else 2)
+    return workspace[p["h_offset"]:p["h_offset"] + nbytes].view(tdt).view(M, I)
+
+
+def forward(x, w_gate_up, w_down, partial_fp32=False, workspace=None, stream=None):
+    """Allocating convenience wrapper around shared_mlp_forward."""
+    odt = torch.float32 if (partial_fp32 or x.dtype == torch.float32) else torch.bfloat16
+    out = torch.empty(x.shape[0], x.shape[1], dtype=odt, device=x.device)
+    return shared_mlp_forward(x, w_gate_up, w_down, out, partial_fp32, workspace, stream)
+
+
+def shared_mlp_set_large_m_threshold(threshold: int) -> int:
+    prev = lib().shared_mlp_set_large_m_threshold(threshold)
+    if prev < 0:
+        _check(8)
+    return prev
+
+
+def shared_mlp_shard_eligible(flag_on, use_sequence_parallel, caller_eligible, tp, H, I) -> bool:
+    return bool(lib().shared_mlp_shard_eligible(int(bool(flag_on)), int(bool(use_sequence_parallel)),
+                                                int(bool(caller_eligible)), int(tp), int(H), int(I)))
+
+
+def shared_mlp_slice_rank(w_gate_up, w_down, w_gate_up_r, w_down_r, tp: int, rank: int, stream=None):
+    two_i, H = w_gate_up.shape
+    I = two_i // 2
+    dt = _dtype_code(w_gate_up)
+    _check(lib().shared_mlp_slice_rank(_ptr(w_gate_up), _ptr(w_down), _ptr(w_gate_up_r), _ptr(w_down_r),
+                                       H, I, tp, rank, dt, _stream(stream, w_gate_up.device)))
+
+
+def shared_mlp_rms_rescale(inp, out, stream=None):
+    M, H = inp.shape
+    if inp.dtype != torch.float32 or out.dtype != torch.bfloat16 or tuple(out.shape) != (M, H):
+        raise ValueError("rescale takes fp32 [M, H] in and bf16 [M, H] out")
+    _check(lib().shared_mlp_rms_rescale(_ptr(inp), _ptr(out), M, H, _stream(stream, inp.device)))

@@ -1,0 +1,366 @@
+// C ABI of libsmlp: host-side validation, M-dispatch planning and kernel dispatch.
+// Every check runs on the host before the first HIP call of an entry point.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+#include "smlp.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Number of compute units the planner sizes grids for (MI355X).
+constexpr int kCUs = 256;
+// The weight-streaming kernels handle up to 128 tokens per call.
+constexpr int64_t kSmallMaxM = 128;
+constexpr int64_t kLimit = (int64_t)1 << 31;
+
+int64_t initial_threshold() {
+  const char* e = std::getenv("SMLP_LARGE_M_MIN");
+  if (e && *e) {
+    char* end = nullptr;
+    long long v = std::strtoll(e, &end, 10);
+    if (end && *end == '\0' && v >= 1 && v <= kSmallMaxM + 1) return (int64_t)v;
+  }
+  return kSmallMaxM + 1;
+}
+std::atomic<int64_t> g_threshold{initial_threshold()};
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SMLP_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Small-M stage plan: feature blocks of 16, 4 waves per workgroup splitting K, and a
+// K-split over workgroups when the feature blocks alone cannot fill the chip.
+smlp::SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
+  smlp::SkinnyPlan sp{};
+  sp.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  sp.nb = 1;
+  sp.waves = 4;
+  const int64_t nblocks = (N + 15) / 16;
+  const int64_t groups = (nblocks + sp.nb - 1) / sp.nb;
+  const int64_t target = kCUs * 3 / 2;
+  int64_t ks = (target + groups - 1) / groups;
+  const int64_t kpairs = (K + 63) / 64;
+  const int64_t max_ks = (kpairs + sp.waves - 1) / sp.waves;  // >= one kpair per wave
+  if (ks > max_ks) ks = max_ks;
+  if (ks < 1) ks = 1;
+  int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
+  ks = (K + kslice - 1) / kslice;
+  sp.ksplit = (int)ks;
+  sp.kslice = (int)kslice;
+  sp.blocks = (int)(groups * ks);
+  return sp;
+}
+
+int out_elem(int dtype, int partial_fp32) { return (dtype == SMLP_FP32 || partial_fp32) ? 4 : 2; }
+
+// Shape/dtype validation and plan; no pointer checks.
+int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp::Plan* p) {
+  if (dtype != SMLP_BF16 && dtype != SMLP_FP32)
+    return fail(SMLP_ERR_DTYPE, "dtype %d is neither SMLP_BF16 (0) nor SMLP_FP32 (1)", dtype);
+  if (M < 0) return fail(SMLP_ERR_SHAPE, "M = %lld < 0", (long long)M);
+  if (H < 1 || I < 1)
+    return fail(SMLP_ERR_SHAPE, "H = %lld and I = %lld must be >= 1", (long long)H, (long long)I);
+  if (H >= kLimit || I >= kLimit || 2 * I * H >= kLimit || M * H >= kLimit || M * I >= kLimit)
+    return fail(SMLP_ERR_SHAPE, "sizes too large: M*H, M*I and 2*I*H must be < 2^31 (M=%lld H=%lld I=%lld)",
+                (long long)M, (long long)H, (long long)I);
+  if (dtype == SMLP_BF16 && (H % 8 || I % 8))
+    return fail(SMLP_ERR_SHAPE, "bf16 needs H %% 8 == 0 and I %% 8 == 0 (H=%lld I=%lld)",
+                (long long)H, (long long)I);
+  std::memset(p, 0, sizeof *p);
+  p->M = M;
+  p->H = H;
+  p->I = I;
+  p->dtype = dtype;
+  p->partial_fp32 = partial_fp32 ? 1 : 0;
+  if (M == 0) {
+    p->path = SMLP_PATH_NONE;
+    p->h_dtype = dtype == SMLP_FP32 ? SMLP_FP32 : SMLP_BF16;
+    return ok();
+  }
+  if (dtype == SMLP_FP32) {
+    p->path = SMLP_PATH_FP32;
+    p->h_dtype = SMLP_FP32;
+    p->h_bytes = round_up((size_t)(M * I) * 4, 256);
+    p->kernels = 2;
+  } else if (M < g_threshold.load() && M <= kSmallMaxM) {
+    p->path = SMLP_PATH_SMALL_M;
+    p->h_dtype = SMLP_FP32;
+    p->h_bytes = round_up((size_t)(M * I) * 4, 256);
+    p->gu = plan_skinny(M, I, H);
+    p->dn = plan_skinny(M, H, I);
+    size_t part = 0;
+    if (p->gu.ksplit > 1) part = (size_t)p->gu.ksplit * M * 2 * I * 4;
+    if (p->dn.ksplit > 1) {
+      size_t d = (size_t)p->dn.ksplit * M * H * 4;
+      if (d > part) part = d;
+    }
+    p->part_bytes = round_up(part, 256);
+    p->kernels = 2 + (p->gu.ksplit > 1) + (p->dn.ksplit > 1);
+  } else {
+    p->path = SMLP_PATH_LARGE_M;
+    p->h_dtype = SMLP_BF16;
+    p->h_bytes = round_up((size_t)(M * I) * 2, 256);
+    const int64_t tiles_m = (M + 127) / 128;
+    p->tgu.bm = 128;
+    p->tgu.bn = 64;
+    p->tgu.blocks = (int)(tiles_m * ((I + 63) / 64));
+    p->tdn.bm = 128;
+    p->tdn.bn = 128;
+    p->tdn.blocks = (int)(tiles_m * ((H + 127) / 128));
+    p->kernels = 2;
+  }
+  p->h_offset = 0;
+  p->part_offset = p->h_bytes;
+  p->workspace_bytes = p->h_bytes + p->part_bytes;
+  return ok();
+}
+
+int check_ptr(const void* ptr, const char* name, size_t align) {
+  if (!ptr) return fail(SMLP_ERR_NULL, "%s is NULL", name);
+  if (!aligned(ptr, align))
+    return fail(SMLP_ERR_ALIGN, "%s = %p is not %zu-byte aligned", name, ptr, align);
+  return SMLP_OK;
+}
+
+int hip_status(int rc, const char* what) {
+  if (rc == hipSuccess) return SMLP_OK;
+  return fail(SMLP_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)rc));
+}
+
+enum Stage { kBoth, kGateUp, kDown };
+
+int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, int64_t M,
+        int64_t H, int64_t I, int dtype, int partial_fp32, void* ws, size_t ws_bytes,
+        hipStream_t stream) {
+  smlp::Plan p;
+  int rc = make_plan(M, H, I, dtype, partial_fp32, &p);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  const size_t al = dtype == SMLP_BF16 ? 16 : 4;
+  const size_t ie = dtype == SMLP_BF16 ? 2 : 4;
+  const size_t oe = (size_t)out_elem(dtype, partial_fp32);
+  const size_t x_n = (size_t)(M * H) * ie, wgu_n = (size_t)(2 * I * H) * ie,
+               wd_n = (size_t)(H * I) * ie, out_n = (size_t)(M * H) * oe;
+  if (stage != kDown) {
+    if ((rc = check_ptr(x, "x", al)) || (rc = check_ptr(wgu, "w_gate_up", al))) return rc;
+  }
+  if (stage != kGateUp) {
+    if ((rc = check_ptr(wd, "w_down", al)) || (rc = check_ptr(out, "out", al))) return rc;
+  }
+  if ((rc = check_ptr(ws, "workspace", 256))) return rc;
+  if (ws_bytes < p.workspace_bytes)
+    return fail(SMLP_ERR_WORKSPACE, "workspace_bytes = %zu < %zu needed", ws_bytes,
+                p.workspace_bytes);
+  if (stage != kDown) {
+    if (overlap(ws, p.workspace_bytes, x, x_n) || overlap(ws, p.workspace_bytes, wgu, wgu_n))
+      return fail(SMLP_ERR_ALIAS, "workspace overlaps x or w_gate_up");
+  }
+  if (stage != kGateUp) {
+    if (overlap(ws, p.workspace_bytes, wd, wd_n))
+      return fail(SMLP_ERR_ALIAS, "workspace overlaps w_down");
+    if (overlap(out, out_n, wd, wd_n) || overlap(out, out_n, ws, p.workspace_bytes) ||
+        (stage == kBoth && (overlap(out, out_n, x, x_n) || overlap(out, out_n, wgu, wgu_n))))
+      return fail(SMLP_ERR_ALIAS, "out overlaps an input or the workspace");
+  }
+
+  (void)hipGetLastError();  // clear stale state so a failure below is attributed to us
+  if (stage != kDown) {
+    switch (p.path) {
+      case SMLP_PATH_FP32:
+        rc = smlp::launch_fp32_gate_up(p, (const float*)x, (const float*)wgu, ws, stream);
+        break;
+      case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_gate_up(p, x, wgu, ws, stream); break;
+      default: rc = smlp::launch_tiled_gate_up(p, x, wgu, ws, stream); break;
+    }
+    if ((rc = hip_status(rc, "gate_up launch"))) return rc;
+  }
+  if (stage != kGateUp) {
+    switch (p.path) {
+      case SMLP_PATH_FP32:
+        rc = smlp::launch_fp32_down(p, (const float*)wd, (float*)out, ws, stream);
+        break;
+      case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_down(p, wd, out, ws, stream); break;
+      default: rc = smlp::launch_tiled_down(p, wd, out, ws, stream); break;
+    }
+    if ((rc = hip_status(rc, "down launch"))) return rc;
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* shared_mlp_status_string(int status) {
+  switch (status) {
+    case SMLP_OK: return "SMLP_OK";
+    case SMLP_ERR_NULL: return "SMLP_ERR_NULL";
+    case SMLP_ERR_SHAPE: return "SMLP_ERR_SHAPE";
+    case SMLP_ERR_ALIGN: return "SMLP_ERR_ALIGN";
+    case SMLP_ERR_ALIAS: return "SMLP_ERR_ALIAS";
+    case SMLP_ERR_WORKSPACE: return "SMLP_ERR_WORKSPACE";
+    case SMLP_ERR_DTYPE: return "SMLP_ERR_DTYPE";
+    case SMLP_ERR_HIP: return "SMLP_ERR_HIP";
+    case SMLP_ERR_ARG: return "SMLP_ERR_ARG";
+    default: return "SMLP_ERR_UNKNOWN";
+  }
+}
+
+const char* shared_mlp_last_error(void) { return g_last_error.c_str(); }
+
+int shared_mlp_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32,
+                    smlp_plan* plan) {
+  if (!plan) return fail(SMLP_ERR_NULL, "plan is NULL");
+  smlp::Plan p;
+  int rc = make_plan(M, H, I, dtype, partial_fp32, &p);
+  if (rc) return rc;
+  plan->path = p.path;
+  plan->h_dtype = p.h_dtype;
+  plan->h_offset = p.h_offset;
+  plan->workspace_bytes = p.workspace_bytes;
+  if (p.path == SMLP_PATH_SMALL_M) {
+    plan->gate_up_ksplit = p.gu.ksplit;
+    plan->down_ksplit = p.dn.ksplit;
+    plan->gate_up_blocks = p.gu.blocks;
+    plan->down_blocks = p.dn.blocks;
+  } else if (p.path == SMLP_PATH_LARGE_M) {
+    plan->gate_up_ksplit = plan->down_ksplit = 1;
+    plan->gate_up_blocks = p.tgu.blocks;
+    plan->down_blocks = p.tdn.blocks;
+  } else {
+    plan->gate_up_ksplit = plan->down_ksplit = 1;
+    plan->gate_up_blocks = plan->down_blocks = 0;
+  }
+  plan->kernels = p.kernels;
+  return ok();
+}
+
+int shared_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int dtype, size_t* bytes) {
+  if (!bytes) return fail(SMLP_ERR_NULL, "bytes is NULL");
+  size_t worst = 0;
+  for (int partial = 0; partial < 2; ++partial) {
+    smlp::Plan p;
+    int rc = make_plan(M, H, I, dtype, partial, &p);
+    if (rc) return rc;
+    if (p.workspace_bytes > worst) worst = p.workspace_bytes;
+  }
+  *bytes = worst;
+  return ok();
+}
+
+int shared_mlp_forward(const void* x, const void* w_gate_up, const void* w_down, void* out,
+                       int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(kBoth, x, w_gate_up, w_down, out, M, H, I, dtype, partial_fp32, workspace,
+             workspace_bytes, stream);
+}
+
+int shared_mlp_gate_up_act(const void* x, const void* w_gate_up, int64_t M, int64_t H,
+                           int64_t I, int dtype, int partial_fp32, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return run(kGateUp, x, w_gate_up, nullptr, nullptr, M, H, I, dtype, partial_fp32, workspace,
+             workspace_bytes, stream);
+}
+
+int shared_mlp_down(const void* w_down, void* out, int64_t M, int64_t H, int64_t I, int dtype,
+                    int partial_fp32, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return run(kDown, nullptr, nullptr, w_down, out, M, H, I, dtype, partial_fp32, workspace,
+             workspace_bytes, stream);
+}
+
+int64_t shared_mlp_set_large_m_threshold(int64_t threshold) {
+  if (threshold < 1 || threshold > kSmallMaxM + 1) {
+    fail(SMLP_ERR_ARG, "threshold %lld outside [1, %lld]", (long long)threshold,
+         (long long)(kSmallMaxM + 1));
+    return -1;
+  }
+  ok();
+  return g_threshold.exchange(threshold);
+}
+
+int shared_mlp_shard_eligible(int flag_on, int use_sequence_parallel, int caller_eligible, int tp,
+                              int64_t H, int64_t I) {
+  return (flag_on && use_sequence_parallel && caller_eligible && tp > 1 && H % tp == 0 &&
+          I % tp == 0)
+             ? 1
+             : 0;
+}
+
+int shared_mlp_slice_rank(const void* w_gate_up, const void* w_down, void* w_gate_up_r,
+                          void* w_down_r, int64_t H, int64_t I, int tp, int rank, int dtype,
+                          hipStream_t stream) {
+  if (dtype != SMLP_BF16 && dtype != SMLP_FP32)
+    return fail(SMLP_ERR_DTYPE, "dtype %d is neither SMLP_BF16 (0) nor SMLP_FP32 (1)", dtype);
+  if (H < 1 || I < 1 || 2 * I * H >= kLimit)
+    return fail(SMLP_ERR_SHAPE, "H = %lld, I = %lld out of range", (long long)H, (long long)I);
+  if (dtype == SMLP_BF16 && (H % 8 || I % 8))
+    return fail(SMLP_ERR_SHAPE, "bf16 needs H %% 8 == 0 and I %% 8 == 0");
+  if (tp < 1 || I % tp || rank < 0 || rank >= tp)
+    return fail(SMLP_ERR_ARG, "rank %d of tp %d does not slice I = %lld", rank, tp, (long long)I);
+  const size_t al = dtype == SMLP_BF16 ? 16 : 4, e = dtype == SMLP_BF16 ? 2 : 4;
+  int rc;
+  if ((rc = check_ptr(w_gate_up, "w_gate_up", al)) || (rc = check_ptr(w_down, "w_down", al)) ||
+      (rc = check_ptr(w_gate_up_r, "w_gate_up_r", al)) ||
+      (rc = check_ptr(w_down_r, "w_down_r", al)))
+    return rc;
+  const int64_t s = I / tp;
+  const size_t ngu = (size_t)(2 * I * H) * e, nwd = (size_t)(H * I) * e,
+               ngu_r = (size_t)(2 * s * H) * e, nwd_r = (size_t)(H * s) * e;
+  if (overlap(w_gate_up_r, ngu_r, w_gate_up, ngu) || overlap(w_gate_up_r, ngu_r, w_down, nwd) ||
+      overlap(w_down_r, nwd_r, w_gate_up, ngu) || overlap(w_down_r, nwd_r, w_down, nwd) ||
+      overlap(w_gate_up_r, ngu_r, w_down_r, nwd_r))
+    return fail(SMLP_ERR_ALIAS, "slice destinations overlap the sources or each other");
+  (void)hipGetLastError();
+  rc = smlp::launch_slice_rank(w_gate_up, w_down, w_gate_up_r, w_down_r, H, I, tp, rank, (int)e,
+                               stream);
+  if ((rc = hip_status(rc, "slice launch"))) return rc;
+  return ok();
+}
+
+int shared_mlp_rms_rescale(const float* in, void* out, int64_t M, int64_t H, hipStream_t stream) {
+  if (M < 0 || H < 4 || H % 4 || M * H >= kLimit || M >= 0x7fffffff)
+    return fail(SMLP_ERR_SHAPE, "rescale needs M >= 0, H >= 4, H %% 4 == 0 (M=%lld H=%lld)",
+                (long long)M, (long long)H);
+  if (M == 0) return ok();
+  int rc;
+  if ((rc = check_ptr(in, "in", 16)) || (rc = check_ptr(out, "out", 16))) return rc;
+  if (overlap(in, (size_t)(M * H) * 4, out, (size_t)(M * H) * 2))
+    return fail(SMLP_ERR_ALIAS, "out overlaps in");
+  (void)hipGetLastError();
+  rc = smlp::launch_rms_rescale(in, (uint16_t*)out, M, H, stream);
+  if ((rc = hip_status(rc, "rescale launch"))) return rc;
+  return ok();
+}
+
+}  // extern "C"

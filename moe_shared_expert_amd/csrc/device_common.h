@@ -1,0 +1,60 @@
+// Device-side helpers shared by the gfx950 kernels of libsmlp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smlp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats -> packed bf16x2 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// SiLU(g) * u in fp32: g * u / (1 + e^-g).  expf of a large positive -g overflows to
+// +inf and gives -0, the correct limit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u / (1.0f + __expf(-g));
+}
+
+// D += A * B for one 16x16x32 bf16 tile.  Lane l holds A[l%16][8*(l/16) .. +7],
+// B[8*(l/16) .. +7][l%16]; D: lane l, element j holds D[4*(l/16)+j][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D += A * B for one 32x32x16 bf16 tile.  Lane l holds A[l%32][8*(l/32) .. +7],
+// B[8*(l/32) .. +7][l%32]; D: lane l, element j holds
+// D[8*(j/4) + 4*(l/32) + j%4][l%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 16-byte global loads.  Weights are read exactly once per call, so they are loaded
+// non-temporally; activations are re-read by many workgroups and use normal loads.
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace smlp

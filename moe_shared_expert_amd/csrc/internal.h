@@ -1,0 +1,58 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smlp {
+
+// One weight-streaming (small-M) stage: out-features in blocks of 16, K split into
+// `ksplit` slices over workgroups and into `waves` slices inside a workgroup.
+struct SkinnyPlan {
+  int mt;        // 16-row token tiles (M <= 16 * mt), one of 1, 2, 4, 8
+  int nb;        // 16-feature output blocks per workgroup
+  int waves;     // waves per workgroup (they split K)
+  int ksplit;    // workgroups along K (1 = no cross-workgroup reduction)
+  int kslice;    // K elements per workgroup slice (multiple of 64)
+  int blocks;    // total workgroups
+};
+
+// One stage of the LDS-tiled MFMA path.
+struct TiledPlan {
+  int bm, bn;    // output tile (rows of x / h, output features)
+  int blocks;
+};
+
+struct Plan {
+  int path;                 // SMLP_PATH_*
+  int64_t M, H, I;
+  int dtype;
+  int partial_fp32;
+  int h_dtype;              // SMLP_FP32 or SMLP_BF16
+  size_t h_offset, h_bytes;
+  size_t part_offset, part_bytes;   // split-K partial sums
+  size_t workspace_bytes;
+  SkinnyPlan gu, dn;
+  TiledPlan tgu, tdn;
+  int kernels;
+};
+
+// Weight-streaming stages (skinny.hip).  Return a hipError_t.
+int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
+                          hipStream_t s);
+int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
+
+// LDS-tiled MFMA stages (tiled.hip).
+int launch_tiled_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
+                         hipStream_t s);
+int launch_tiled_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
+
+// fp32 stages and helpers (aux.hip).
+int launch_fp32_gate_up(const Plan& p, const float* x, const float* w_gate_up, void* ws,
+                        hipStream_t s);
+int launch_fp32_down(const Plan& p, const float* w_down, float* out, void* ws, hipStream_t s);
+int launch_slice_rank(const void* wgu, const void* wd, void* wgu_r, void* wd_r, int64_t H,
+                      int64_t I, int tp, int rank, int elem_bytes, hipStream_t s);
+int launch_rms_rescale(const float* in, uint16_t* out, int64_t M, int64_t H, hipStream_t s);
+
+}  // namespace smlp

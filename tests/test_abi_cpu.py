@@ -1,0 +1,172 @@
+"""Host-only tests of libsmlp's C ABI: exports, validation, planning, gating.
+
+No GPU is needed: every call here either fails validation (which happens on the
+host before any HIP call) or is a pure host function.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import oracle
+from conftest import GOLDEN, ROOT
+
+binding = pytest.importorskip("moe_shared_expert_amd.binding")
+
+H, I = 7168, 6144
+BF16, FP32 = binding.SMLP_BF16, binding.SMLP_FP32
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libsmlp.so is not built (python -m moe_shared_expert_amd.build)")
+    return binding.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "smlp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(shared_mlp_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding.EXPORTS), "binding and header disagree"
+
+
+def test_status_strings(L):
+    for code, name in enumerate(["SMLP_OK", "SMLP_ERR_NULL", "SMLP_ERR_SHAPE", "SMLP_ERR_ALIGN",
+                                 "SMLP_ERR_ALIAS", "SMLP_ERR_WORKSPACE", "SMLP_ERR_DTYPE",
+                                 "SMLP_ERR_HIP", "SMLP_ERR_ARG"]):
+        assert L.shared_mlp_status_string(code).decode() == name
+    assert L.shared_mlp_status_string(99).decode() == "SMLP_ERR_UNKNOWN"
+
+
+# Fake, never dereferenced device addresses, far apart and 256-byte aligned.
+GB = 1 << 30
+X, WGU, WD, OUT, WS = (0x7f0000000000 + k * 4 * GB for k in range(5))
+
+
+def _ws(m, h, i, dt=BF16):
+    return binding.shared_mlp_workspace_bytes(m, h, i, dt)
+
+
+def _fwd(L, x=X, wgu=WGU, wd=WD, out=OUT, m=16, h=H, i=I, dt=BF16, partial=0, ws=WS, wsb=None):
+    if wsb is None:
+        try:
+            wsb = _ws(m, h, i, dt)
+        except binding.SmlpError:
+            wsb = 1 << 40
+    return L.shared_mlp_forward(x, wgu, wd, out, m, h, i, dt, partial, ws, wsb, None)
+
+
+def test_forward_validation_codes(L):
+    assert _fwd(L, dt=7) == 6                      # dtype
+    assert _fwd(L, m=-1) == 2                      # shape
+    assert _fwd(L, h=0) == 2
+    assert _fwd(L, i=0) == 2
+    assert _fwd(L, h=7170) == 2                    # bf16 needs H % 8
+    assert _fwd(L, i=6148) == 2                    # bf16 needs I % 8
+    assert _fwd(L, m=1 << 20, h=4096, i=64) == 2   # M*H >= 2^31
+    assert _fwd(L, x=0) == 1                       # null
+    assert _fwd(L, wgu=0) == 1
+    assert _fwd(L, wd=0) == 1
+    assert _fwd(L, out=0) == 1
+    assert _fwd(L, ws=0) == 1
+    assert _fwd(L, x=X + 8) == 3                   # bf16 needs 16-byte alignment
+    assert _fwd(L, out=OUT + 2) == 3
+    assert _fwd(L, ws=WS + 16) == 3                # workspace 256-byte aligned
+    assert _fwd(L, wsb=_ws(16, H, I) - 1) == 5     # workspace too small
+    assert _fwd(L, out=X) == 4                     # out aliases x
+    assert _fwd(L, out=WGU + 1024) == 4            # out inside w_gate_up
+    assert _fwd(L, out=WS) == 4                    # out aliases the workspace
+    assert _fwd(L, ws=WD) == 4                     # workspace aliases w_down
+    # fp32 inputs: any sizes, 4-byte alignment; misalignment below 4 still fails
+    assert _fwd(L, dt=FP32, x=X + 2, m=3, h=5, i=3) == 3
+    assert "alignment" in L.shared_mlp_last_error().decode() or "aligned" in L.shared_mlp_last_error().decode()
+
+
+def test_m_zero_is_a_noop(L):
+    # M == 0 returns OK before touching a pointer or the GPU
+    assert L.shared_mlp_forward(None, None, None, None, 0, H, I, BF16, 0, None, 0, None) == 0
+    assert L.shared_mlp_last_error().decode() == ""
+
+
+def test_stage_entry_points_validate(L):
+    wsb = _ws(16, H, I)
+    assert L.shared_mlp_gate_up_act(0, WGU, 16, H, I, BF16, 0, WS, wsb, None) == 1
+    assert L.shared_mlp_gate_up_act(X, WGU, 16, H, I, BF16, 0, X, wsb, None) == 4
+    assert L.shared_mlp_down(WD, OUT, 16, H, I, BF16, 0, WS, 0, None) == 5
+    assert L.shared_mlp_down(WD, WS, 16, H, I, BF16, 0, WS, wsb, None) == 4
+
+
+def test_workspace_and_plan(L):
+    p = binding.shared_mlp_plan(16, H, I)
+    assert p["path_name"] == "small_m" and p["h_dtype"] == FP32
+    assert p["workspace_bytes"] >= 16 * I * 4
+    p = binding.shared_mlp_plan(8192, H, I)
+    assert p["path_name"] == "large_m" and p["h_dtype"] == BF16
+    assert p["workspace_bytes"] >= 8192 * I * 2
+    p = binding.shared_mlp_plan(12, 16, 12, FP32)
+    assert p["path_name"] == "fp32"
+    p = binding.shared_mlp_plan(0, H, I)
+    assert p["path_name"] == "none" and p["kernels"] == 0
+    # the TP-shard shapes need a K split to fill the chip
+    p = binding.shared_mlp_plan(128, H, 384, BF16, True)
+    assert p["gate_up_ksplit"] > 1
+    assert p["workspace_bytes"] <= binding.shared_mlp_workspace_bytes(128, H, 384, BF16)
+
+
+def test_threshold_setter(L):
+    prev = binding.shared_mlp_set_large_m_threshold(64)
+    try:
+        assert binding.shared_mlp_plan(64, H, I)["path_name"] == "large_m"
+        assert binding.shared_mlp_plan(63, H, I)["path_name"] == "small_m"
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_set_large_m_threshold(0)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_set_large_m_threshold(1 << 20)
+    finally:
+        binding.shared_mlp_set_large_m_threshold(prev)
+
+
+def test_shard_eligible_matches_oracle_exhaustively(L):
+    for flag, sp, ok, tp, hid, inter in itertools.product(
+            (0, 1), (0, 1), (0, 1), (0, 1, 2, 3, 4, 5, 8, 16), (16, 7168, 7170), (12, 6144, 6148)):
+        assert binding.shared_mlp_shard_eligible(flag, sp, ok, tp, hid, inter) == \
+            oracle.shard_sequence_parallel_mlp(flag, sp, ok, tp, hid, inter)
+
+
+def test_shard_eligible_golden_cases(L):
+    with open(os.path.join(GOLDEN, "gating_cases.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for flag, sp, ok, tp, hid, inter, expect, label in rows:
+        assert binding.shared_mlp_shard_eligible(int(flag), int(sp), int(ok), int(tp), int(hid),
+                                                 int(inter)) == bool(int(expect)), label
+
+
+def test_slice_rank_validation(L):
+    s = L.shared_mlp_slice_rank
+    assert s(WGU, WD, OUT, WS, H, I, 8, 8, BF16, None) == 8      # rank out of range
+    assert s(WGU, WD, OUT, WS, H, I, 5, 0, BF16, None) == 8      # 6144 % 5 != 0
+    assert s(WGU, WD, OUT, WS, H, I, 0, 0, BF16, None) == 8
+    assert s(0, WD, OUT, WS, H, I, 8, 0, BF16, None) == 1
+    assert s(WGU, WD, WGU, WS, H, I, 8, 0, BF16, None) == 4      # dest aliases source
+    assert s(WGU, WD, OUT, OUT + 64, H, I, 8, 0, BF16, None) == 4  # dests overlap
+    assert s(WGU, WD, OUT, WS, H, I, 8, 0, 3, None) == 6
+
+
+def test_rescale_validation(L):
+    r = L.shared_mlp_rms_rescale
+    assert r(X, OUT, 128, 7170, None) == 2
+    assert r(X, OUT, -1, H, None) == 2
+    assert r(0, OUT, 128, H, None) == 1
+    assert r(X + 4, OUT, 128, H, None) == 3
+    assert r(X, X + 64, 128, H, None) == 4
+    assert r(None, None, 0, H, None) == 0

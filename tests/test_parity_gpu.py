@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: max|err| <= 2e-2 * RMS(ref) for bf16 inputs with fp32 accumulation
+(RMS over all elements of the oracle output of that call), and <= 1e-5 * RMS(ref)
+for fp32 inputs.  Inputs are the seeded synthetic tensors of ``synth``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import (BF16_TOL, DEV, FP32_TOL, H, I, assert_rms_close, f64, rms,
+                         workspace_for)
+
+pytestmark = pytest.mark.gpu
+
+binding = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global binding
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from moe_shared_expert_amd import binding as b
+    b.lib()  # fails loudly if libsmlp.so is missing
+    binding = b
+
+
+def run_forward(x, wgu, wd, partial=False):
+    M, Hh = x.shape
+    Ii = wgu.shape[0] // 2
+    dt = binding.SMLP_FP32 if x.dtype == torch.float32 else binding.SMLP_BF16
+    odt = torch.float32 if (partial or x.dtype == torch.float32) else torch.bfloat16
+    out = torch.empty(M, Hh, dtype=odt, device=DEV)
+    ws = workspace_for(M, Hh, Ii, dt)
+    binding.shared_mlp_forward(x, wgu, wd, out, partial_fp32=partial, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def slice_on_gpu(wgu, wd, tp, r):
+    two_i, Hh = wgu.shape
+    s = two_i // 2 // tp
+    wgu_r = torch.empty(2 * s, Hh, dtype=wgu.dtype, device=DEV)
+    wd_r = torch.empty(Hh, s, dtype=wd.dtype, device=DEV)
+    binding.shared_mlp_slice_rank(wgu, wd, wgu_r, wd_r, tp, r)
+    torch.cuda.synchronize()
+    return wgu_r, wd_r
+
+
+# ---------------------------------------------------------------- tiny fp32 case
+def test_tiny_fp32_replicated_and_slices():
+    x, gate, up, down, tp, t = synth.tiny_fp32_case()
+    wgu = synth.merged_gate_up(gate, up)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(down))
+    xd, wgud, wdd = x.to(DEV), wgu.to(DEV), down.to(DEV)
+    rep = run_forward(xd, wgud, wdd)
+    assert_rms_close(rep, ref, FP32_TOL, "tiny fp32 replicated")
+    total = np.zeros_like(ref)
+    for r in range(tp):
+        wgu_r, wd_r = slice_on_gpu(wgud, wdd, tp, r)
+        ref_r = oracle.rank_partial(f64(x), f64(wgu), f64(down), tp, r)
+        part = run_forward(xd, wgu_r, wd_r, partial=True)
+        assert_rms_close(part, ref_r, FP32_TOL, f"tiny fp32 partial r{r}")
+        total += f64(part)
+    # sum of partials over the 4 slices reproduces the replicated output, per token shard
+    r_all = rms(ref)
+    for r in range(tp):
+        mine = oracle.rank_token_rows(total, tp, r)
+        err = np.abs(mine - ref[r * t:(r + 1) * t]).max()
+        assert err <= FP32_TOL * r_all, (r, err)
+    # the pages' own check, reported in their terms (fp32, atol = rtol = 1e-5)
+    torch.testing.assert_close(torch.from_numpy(total).float(), rep.cpu(), atol=1e-5, rtol=1e-5)
+
+
+# ------------------------------------------------------- replicated decode, M = 16
+@pytest.fixture(scope="module")
+def x16():
+    return synth.activations(16, H, config=2)
+
+
+@pytest.mark.parametrize("copy", range(8))
+def test_decode_replicated_m16(copy, x16):
+    wgu, wd = synth.layer_weights(H, I, config=2, copy=copy)
+    out = run_forward(x16.to(DEV), wgu.to(DEV), wd.to(DEV))
+    assert out.dtype == torch.bfloat16
+    ref = oracle.swiglu_mlp(f64(x16), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, f"rep M=16 copy{copy}")
+
+
+# -------------------------------------------------------------- TP8 shard, M = 128
+@pytest.mark.parametrize("copy", range(2))
+def test_tp8_shard_partial(copy):
+    x = synth.activations(128, H, config=3)
+    wgu, wd = synth.layer_weights(H, 768, config=3, copy=copy, fan_in_down=I)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=True)
+    assert out.dtype == torch.float32
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, f"tp8 partial copy{copy}")
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    wgu, wd = synth.layer_weights(H, I, config=5, copy=0)
+    return wgu, wd, f64(wgu), f64(wd)
+
+
+def test_tp8_slices_sum_to_replicated(full_layer):
+    wgu, wd, wgu64, wd64 = full_layer
+    x = synth.activations(128, H, config=3, copy=1)
+    x64 = f64(x)
+    xd, wgud, wdd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+    ref = oracle.swiglu_mlp(x64, wgu64, wd64)
+    tp = 8
+    total = np.zeros_like(ref)
+    for r in range(tp):
+        wgu_r, wd_r = slice_on_gpu(wgud, wdd, tp, r)
+        g_r, d_r = oracle.rank_shard(wgu64, wd64, tp, r)
+        assert np.array_equal(f64(wgu_r), g_r) and np.array_equal(f64(wd_r), d_r), "slice not exact"
+        part = run_forward(xd, wgu_r, wd_r, partial=True)
+        assert_rms_close(part, oracle.swiglu_mlp(x64, g_r, d_r), BF16_TOL, f"tp8 slice r{r}")
+        total += f64(part)
+    assert_rms_close(torch.from_numpy(total), ref, BF16_TOL, "tp8 sum of 8 slices vs replicated")
+    # disjoint token shards: rank r keeps rows r*16..(r+1)*16 of the summed result
+    for r in range(tp):
+        mine = oracle.rank_token_rows(total, tp, r)
+        assert np.abs(mine - ref[r * 16:(r + 1) * 16]).max() <= BF16_TOL * rms(ref)
+
+
+# ------------------------------------------------- 92-layer TP16 stack, M = 128
+N_LAYERS = 92
+
+
+@pytest.fixture(scope="module")
+def stack92():
+    return [synth.layer_weights(H, 384, config=4, copy=l, fan_in_down=I) for l in range(N_LAYERS)]
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_stack92_every_layer_on_seeded_input(stack92, chunk):
+    # each layer's kernel output against the oracle, on a seeded unit-RMS input
+    for l in range(chunk * 23, (chunk + 1) * 23):
+        wgu, wd = stack92[l]
+        x = synth.activations(128, H, config=4, copy=l)
+        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=True)
+        ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+        assert_rms_close(out, ref, BF16_TOL, f"stack92 layer{l}")
+
+
+def test_stack92_chain_properties(stack92):
+    # The chained run (output rescaled to unit RMS feeds the next layer).  The chain
+    # amplifies rounding differences, so it is checked by properties at every layer:
+    # each layer input has unit RMS per row up to bf16 rounding, outputs are finite.
+    dev_w = [(g.to(DEV), d.to(DEV)) for g, d in stack92]
+    x = synth.activations(128, H, config=4).to(DEV)
+    out = torch.empty(128, H, dtype=torch.float32, device=DEV)
+    ws = workspace_for(128, H, 384, binding.SMLP_BF16)
+    for l, (g, d) in enumerate(dev_w):
+        binding.shared_mlp_forward(x, g, d, out, partial_fp32=True, workspace=ws)
+        nxt = torch.empty(128, H, dtype=torch.bfloat16, device=DEV)
+        binding.shared_mlp_rms_rescale(out, nxt)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), l
+        row_rms = nxt.float().pow(2).mean(dim=1).sqrt()
+        assert (row_rms - 1).abs().max().item() < 4e-3, (l, row_rms)
+        x = nxt
+
+
+def test_rms_rescale_against_oracle():
+    a = synth.normal((128, H), 0.3, seed=4242, dtype=torch.float32)
+    a[5] *= 100.0
+    a[7] *= 1e-3
+    out = torch.empty(128, H, dtype=torch.bfloat16, device=DEV)
+    binding.shared_mlp_rms_rescale(a.to(DEV), out)
+    torch.cuda.synchronize()
+    ref = oracle.rms_rescale_rows(f64(a))
+    # one bf16 rounding (relative half-ulp 2^-8) plus fp32 arithmetic
+    err = np.abs(f64(out) - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert err.max() <= 2.0 ** -8 * 1.01
+
+
+# ------------------------------------------------------------ prefill, M = 8192
+SAMPLE_ROWS = [0, 1, 2, 15, 16, 127, 128, 129, 1000, 4095, 4096, 8190, 8191] + list(range(3001, 8000, 419))
+
+
+def test_prefill_m8192_sampled_rows(full_layer):
+    wgu, wd, wgu64, wd64 = full_layer
+    x = synth.activations(8192, H, config=5)
+    p = binding.shared_mlp_plan(8192, H, I)
+    assert p["path_name"] == "large_m"
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
+    rows = np.array(SAMPLE_ROWS)
+    ref = oracle.swiglu_mlp(f64(x[rows]), wgu64, wd64)
+    # RMS of the oracle over the sampled rows stands in for the full-output RMS
+    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, "prefill M=8192 sampled")
+
+
+# ---------------------------------------------- M sweep, replicated and TP8 shard
+@pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 2048])
+def test_sweep_replicated(M, full_layer):
+    wgu, wd, wgu64, wd64 = full_layer
+    x = synth.activations(M, H, config=5, copy=M)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
+    rows = np.arange(M) if M <= 512 else np.array(sorted(set([0, M - 1] + list(range(1, M, M // 24)))))
+    ref = oracle.swiglu_mlp(f64(x[rows]), wgu64, wd64)
+    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"sweep rep M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 2048])
+def test_sweep_tp8(M, full_layer):
+    wgu, wd, wgu64, wd64 = full_layer
+    g_r, d_r = oracle.rank_shard(wgu64, wd64, 8, 5)
+    x = synth.activations(M, H, config=5, copy=10000 + M)
+    wgu_r, wd_r = slice_on_gpu(wgu.to(DEV), wd.to(DEV), 8, 5)
+    out = run_forward(x.to(DEV), wgu_r, wd_r, partial=True)
+    rows = np.arange(M) if M <= 512 else np.array(sorted(set([0, M - 1] + list(range(1, M, M // 24)))))
+    ref = oracle.swiglu_mlp(f64(x[rows]), g_r, d_r)
+    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"sweep tp8 M={M}")
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("M", [1, 3, 13, 16, 17, 33, 64, 65, 100, 127, 128, 129, 200, 255, 300])
+@pytest.mark.parametrize("partial", [False, True])
+def test_ragged_m_medium_shapes(M, partial):
+    Hh, Ii = 1024, 768
+    x = synth.activations(M, Hh, config=7, copy=M)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=7)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=partial)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, f"ragged M={M} partial={partial}")
+
+
+@pytest.mark.parametrize("Hh,Ii", [(136, 40), (72, 8), (8, 24), (520, 1000)])
+@pytest.mark.parametrize("M", [1, 7, 130])
+def test_ragged_feature_sizes(Hh, Ii, M):
+    x = synth.activations(M, Hh, config=8, copy=M)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=8)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=True)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, f"ragged H={Hh} I={Ii} M={M}")
+
+
+@pytest.mark.parametrize("M", [16, 64, 128])
+def test_both_paths_agree_with_oracle(M):
+    Hh, Ii = 2048, 1536
+    x = synth.activations(M, Hh, config=9, copy=M)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=9)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+    small = run_forward(xd, gd, dd)
+    prev = binding.shared_mlp_set_large_m_threshold(1)
+    try:
+        assert binding.shared_mlp_plan(M, Hh, Ii)["path_name"] == "large_m"
+        large = run_forward(xd, gd, dd)
+    finally:
+        binding.shared_mlp_set_large_m_threshold(prev)
+    assert_rms_close(small, ref, BF16_TOL, f"small path M={M}")
+    assert_rms_close(large, ref, BF16_TOL, f"large path M={M}")
+
+
+def test_m_zero_leaves_output_untouched():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    wgu = torch.zeros(2 * 32, 64, dtype=torch.bfloat16, device=DEV)
+    wd = torch.zeros(64, 32, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    binding.shared_mlp_forward(x, wgu, wd, out)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1, 12, 16, 128, 300])
+def test_guard_bands_untouched(M):
+    Hh, Ii = 1024, 768
+    x = synth.activations(M, Hh, config=10, copy=M).to(DEV)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=10)
+    wgu, wd = wgu.to(DEV), wd.to(DEV)
+    for partial in (False, True):
+        dt = torch.float32 if partial else torch.bfloat16
+        guard = 4096
+        buf = torch.full((M * Hh + 2 * guard,), float("nan"), dtype=dt, device=DEV)
+        out = buf[guard:guard + M * Hh].view(M, Hh)
+        ws = workspace_for(M, Hh, Ii, binding.SMLP_BF16)
+        binding.shared_mlp_forward(x, wgu, wd, out, partial_fp32=partial, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * Hh:]).all()
+        assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("M", [16, 128, 1024])
+def test_deterministic_bits(M):
+    Hh, Ii = 2048, 1536
+    x = synth.activations(M, Hh, config=11).to(DEV)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=11)
+    wgu, wd = wgu.to(DEV), wd.to(DEV)
+    a = run_forward(x, wgu, wd)
+    b = run_forward(x, wgu, wd)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_row_independence_small_path():
+    Hh, Ii = 2048, 1536
+    x = synth.activations(16, Hh, config=12).to(DEV)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=12)
+    wgu, wd = wgu.to(DEV), wd.to(DEV)
+    full = run_forward(x, wgu, wd, partial=True)
+    for t in (0, 7, 15):
+        one = run_forward(x[t:t + 1].contiguous(), wgu, wd, partial=True)
+        # same kernel shape for M = 1 and M = 16: identical accumulation order
+        assert torch.equal(one[0], full[t])
+
+
+@pytest.mark.parametrize("M", [16, 128, 512])
+def test_stage_entry_points(M):
+    Hh, Ii = 2048, 1536
+    x = synth.activations(M, Hh, config=13, copy=M)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=13)
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+    ws = workspace_for(M, Hh, Ii, binding.SMLP_BF16)
+    binding.shared_mlp_gate_up_act(xd, gd, ws)
+    torch.cuda.synchronize()
+    h = binding.read_h(ws, M, Ii, Hh).clone()
+    h_ref = oracle.gate_up_act(f64(x), f64(wgu))
+    assert_rms_close(h, h_ref, BF16_TOL, f"stage gate_up_act M={M}")
+    out = torch.empty(M, Hh, dtype=torch.bfloat16, device=DEV)
+    binding.shared_mlp_down(dd, out, ws)
+    torch.cuda.synchronize()
+    whole = run_forward(xd, gd, dd)
+    assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
+
+
+def test_slice_rank_fp32_bit_exact():
+    r_ = np.random.Generator(np.random.PCG64(5))
+    wgu = torch.from_numpy(r_.standard_normal((2 * 24, 20)).astype(np.float32))
+    wd = torch.from_numpy(r_.standard_normal((20, 24)).astype(np.float32))
+    for tp in (1, 2, 3, 8):
+        for r in range(tp):
+            g, d = slice_on_gpu(wgu.to(DEV), wd.to(DEV), tp, r)
+            eg, ed = oracle.rank_shard(f64(wgu), f64(wd), tp, r)
+            assert np.array_equal(f64(g), eg) and np.array_equal(f64(d), ed)
