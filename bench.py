@@ -57,58 +57,76 @@ def make_inputs(M, I_r, copies, cfg, dev):
     return x, ws
 
 
-def run_workload(name, steps, warmup, dev, per_kernel=True):
+def run_workload(name, steps, warmup, dev, launch="graph"):
+    """Time `steps` layer forwards (value) and, separately, `steps` launches of the
+    dominant gate_up stage each bracketed by its own event pair (roofline)."""
     M, I_r, partial, copies, cfg, desc = WORKLOADS[name]
     x, weights = make_inputs(M, I_r, copies, cfg, dev)
     odt = torch.float32 if partial else torch.bfloat16
     out = torch.empty(M, H, dtype=odt, device=dev)
     wsb = binding.shared_mlp_workspace_bytes(M, H, I_r, binding.SMLP_BF16)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
     plan = binding.shared_mlp_plan(M, H, I_r, binding.SMLP_BF16, partial)
 
-    def step(i, evs=None):
+    def step(i, stream):
         g, d = weights[i % copies]
-        if evs is None:
-            binding.shared_mlp_forward(x, g, d, out, partial, ws, stream)
-        else:
-            evs[0].record(stream)
-            binding.shared_mlp_gate_up_act(x, g, ws, partial, stream)
-            evs[1].record(stream)
-            binding.shared_mlp_down(d, out, ws, partial, stream)
+        binding.shared_mlp_forward(x, g, d, out, partial, ws, stream)
 
-    for i in range(warmup):
-        step(i)
+    stream = torch.cuda.Stream(dev) if launch == "graph" else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, copies)):
+            step(i, stream)
     torch.cuda.synchronize()
-    # Timed region: K steps; each step is the two stage calls with an event pair around
-    # the dominant (gate_up) kernel(s).
-    kev = [(_ev(), _ev()) for _ in range(steps)] if per_kernel else None
+    graph = None
+    if launch == "graph":
+        # one replay = one pass over every weight copy
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(copies):
+                    step(i, stream)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    reps = max(1, steps // copies) if graph is not None else 0
+    n_steps = reps * copies if graph is not None else steps
     t0, t1 = _ev(), _ev()
     torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(steps):
-        step(i, kev[i] if per_kernel else None)
-    t1.record(stream)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        if graph is not None:
+            for _ in range(reps):
+                graph.replay()
+        else:
+            for i in range(steps):
+                step(i, stream)
+        t1.record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    gu_us = None
-    if per_kernel:
-        gu_us = 1e3 * sum(a.elapsed_time(b) for a, b in kev) / steps
+    ms = t0.elapsed_time(t1) / n_steps
+
+    # dominant kernel: gate_up + SiLU-and-mul, each launch between its own events
+    kev = [(_ev(), _ev()) for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            g, _ = weights[i % copies]
+            kev[i][0].record(stream)
+            binding.shared_mlp_gate_up_act(x, g, ws, partial, stream)
+            kev[i][1].record(stream)
+    torch.cuda.synchronize()
+    gu_us = 1e3 * sum(a.elapsed_time(b) for a, b in kev) / steps
+
     out_elem = 4 if partial else 2
     alg = roofline.algorithmic_bytes(M, H, I_r, 2, out_elem)
     fl = roofline.flops(M, H, I_r)
-    res = {
+    h_elem = {binding.SMLP_FP32: 4, binding.SMLP_BF16_HILO: 4, binding.SMLP_BF16: 2}[plan["h_dtype"]]
+    gu_alg = roofline.gate_up_bytes(H, I_r) + M * H * 2 + M * I_r * h_elem
+    return {
         "name": name, "desc": desc, "M": M, "I_r": I_r, "partial": partial, "copies": copies,
+        "steps": n_steps, "launch": launch,
         "ms_per_step": ms, "us_per_layer": ms * 1e3, "alg_bytes": alg, "flops": fl,
         "gbs": alg / (ms * 1e-3) / 1e9, "tflops": fl / (ms * 1e-3) / 1e12, "plan": plan,
+        "gate_up_us": gu_us, "gate_up_alg_bytes": gu_alg, "gate_up_gbs": gu_alg / (gu_us * 1e-6) / 1e9,
     }
-    if gu_us is not None:
-        h_bytes = M * I_r * (4 if plan["h_dtype"] == binding.SMLP_FP32 else 2)
-        gu_alg = roofline.gate_up_bytes(H, I_r) + M * H * 2 + h_bytes
-        res["gate_up_us"] = gu_us
-        res["gate_up_alg_bytes"] = gu_alg
-        res["gate_up_gbs"] = gu_alg / (gu_us * 1e-6) / 1e9
-    return res
 
 
 def cpu_baseline(name, budget_s=12.0):
@@ -151,6 +169,8 @@ def main():
     ap.add_argument("--workload", default="decode_rep_m16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also print the M sweep lines")
+    ap.add_argument("--launch", default="graph", choices=("graph", "eager"),
+                    help="replay the steps from a captured hipGraph (default) or launch eagerly")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path "
@@ -158,16 +178,17 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     binding.lib()
-    r = run_workload(args.workload, args.steps, args.warmup, dev)
+    r = run_workload(args.workload, args.steps, args.warmup, dev, args.launch)
     line = {
         "metric": METRIC, "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": r["desc"], "M": r["M"], "H": H, "I": r["I_r"],
                    "layout": "tp-shard" if r["partial"] else "replicated",
                    "out": "fp32 partial" if r["partial"] else "bf16",
-                   "weight_copies": r["copies"], "path": r["plan"]["path_name"]},
+                   "weight_copies": r["copies"], "path": r["plan"]["path_name"],
+                   "launch": "hipGraph replay" if r["launch"] == "graph" else "eager"},
         "us_per_layer": round(r["us_per_layer"], 3),
         "hbm_frac": round(r["gbs"] / roofline.HBM_PEAK_GBS, 4),
         "tflops": round(r["tflops"], 2),

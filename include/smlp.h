@@ -50,8 +50,9 @@
 extern "C" {
 #endif
 
-/* Element types. */
-enum { SMLP_BF16 = 0, SMLP_FP32 = 1 };
+/* Element types.  SMLP_BF16_HILO only describes the intermediate h in a workspace:
+ * two bf16 planes [M, I] (hi first, then lo) whose sum is the fp32 value. */
+enum { SMLP_BF16 = 0, SMLP_FP32 = 1, SMLP_BF16_HILO = 2 };
 
 /* Status codes. */
 enum {

@@ -15,7 +15,7 @@ import os
 
 import torch
 
-SMLP_BF16, SMLP_FP32 = 0, 1
+SMLP_BF16, SMLP_FP32, SMLP_BF16_HILO = 0, 1, 2
 PATH_NAMES = {0: "none", 1: "fp32", 2: "small_m", 3: "large_m"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +55,10 @@ EXPORTS = {
     "shared_mlp_slice_rank": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "shared_mlp_rms_rescale": (_int, [_vp, _vp, _i64, _i64, _vp]),
 }
+# declared in include/smlp_tuning.h
+TUNING_EXPORTS = {
+    "shared_mlp_tune_skinny": (_int, [_int, _int, _int, _int, _int, _int]),
+}
 
 
 def lib():
@@ -65,7 +69,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m moe_shared_expert_amd.build` (no fallback exists)")
         L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in EXPORTS.items():
+        for name, (res, args) in {**EXPORTS, **TUNING_EXPORTS}.items():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
@@ -165,11 +169,22 @@ def shared_mlp_down(w_down, out, workspace, partial_fp32=False, stream=None):
 
 
 def read_h(workspace, M: int, I: int, H: int, dtype: int = SMLP_BF16, partial_fp32=False):
-    """View of the intermediate h [M, I] inside a workspace (after shared_mlp_gate_up_act)."""
+    """The intermediate h [M, I] held in a workspace (after shared_mlp_gate_up_act), as
+    stored (fp32 or bf16) or, for two bf16 planes, their fp32 sum."""
     p = shared_mlp_plan(M, H, I, dtype, partial_fp32)
-    tdt = torch.float32 if p["h_dtype"] == SMLP_FP32 else torch.bfloat16
-    nbytes = M * I * (4 if tdt == torch.float32 else 2)
-    return workspace[p["h_offset"]:p["h_offset"] + nbytes].view(tdt).view(M, I)
+    o = p["h_offset"]
+    if p["h_dtype"] == SMLP_FP32:
+        return workspace[o:o + 4 * M * I].view(torch.float32).view(M, I)
+    if p["h_dtype"] == SMLP_BF16_HILO:
+        planes = workspace[o:o + 4 * M * I].view(torch.bfloat16).view(2, M, I)
+        return planes[0].float() + planes[1].float()
+    return workspace[o:o + 2 * M * I].view(torch.bfloat16).view(M, I)
+
+
+def shared_mlp_tune_skinny(stage: int, kind: int = 0, nb: int = 0, waves: int = 0, u: int = 0,
+                           ksplit: int = 0):
+    """Pin small-M planner parameters (0 = automatic); see include/smlp_tuning.h."""
+    _check(lib().shared_mlp_tune_skinny(stage, kind, nb, waves, u, ksplit))
 
 
 def forward(x, w_gate_up, w_down, partial_fp32=False, workspace=None, stream=None):

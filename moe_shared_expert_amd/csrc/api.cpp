@@ -11,6 +11,7 @@
 
 #include "internal.h"
 #include "smlp.h"
+#include "smlp_tuning.h"
 
 namespace {
 
@@ -58,27 +59,71 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Small-M stage plan: feature blocks of 16, 4 waves per workgroup splitting K, and a
-// K-split over workgroups when the feature blocks alone cannot fill the chip.
-smlp::SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
+// Tuning overrides of the small-M planner (0 = automatic), per stage.
+struct SkinnyOverride {
+  std::atomic<int> kind{0}, nb{0}, waves{0}, u{0}, ksplit{0};
+};
+SkinnyOverride g_tune[2];
+
+// Small-M stage plan.  M <= 32: the LDS-staged kernel, one workgroup per compute unit
+// over an equal contiguous share of the features (gate_up) or rows (down), the whole K
+// range, waves interleaved over K.  M > 32: the direct-load kernel over 16-feature
+// blocks, with a K split over workgroups when the blocks alone cannot keep about
+// three waves per compute unit streaming.  Returns false if a pinned (tuned)
+// configuration is not one of the compiled kernels.
+bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* out) {
+  using namespace smlp;
+  const SkinnyOverride& o = g_tune[stage];
   smlp::SkinnyPlan sp{};
+  sp.kind = o.kind.load() ? o.kind.load() : (M <= 32 ? SKINNY_LDS16 : SKINNY_DIRECT16);
+  if (sp.kind == SKINNY_LDS16 && M > 32) return false;
   sp.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  sp.nb = 1;
-  sp.waves = 4;
-  const int64_t nblocks = (N + 15) / 16;
-  const int64_t groups = (nblocks + sp.nb - 1) / sp.nb;
-  const int64_t target = kCUs * 3 / 2;
-  int64_t ks = (target + groups - 1) / groups;
-  const int64_t kpairs = (K + 63) / 64;
-  const int64_t max_ks = (kpairs + sp.waves - 1) / sp.waves;  // >= one kpair per wave
-  if (ks > max_ks) ks = max_ks;
-  if (ks < 1) ks = 1;
-  int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
-  ks = (K + kslice - 1) / kslice;
-  sp.ksplit = (int)ks;
-  sp.kslice = (int)kslice;
-  sp.blocks = (int)(groups * ks);
-  return sp;
+  sp.u = o.u.load() ? o.u.load() : 1;
+  const int64_t ksteps = (K + 63) / 64;
+  if (sp.kind == SKINNY_LDS16) {
+    const int64_t tile = stage == 0 ? 8 : 16;  // features per 16-row tile
+    int64_t groups = o.nb.load() ? (N + tile * o.nb.load() - 1) / (tile * o.nb.load()) : kCUs;
+    if (groups > N) groups = N;
+    int64_t fpw = (N + groups - 1) / groups;
+    int64_t nt = (fpw + tile - 1) / tile;
+    if (nt > 4) {
+      nt = 4;
+      fpw = 4 * tile;
+    }
+    groups = (N + fpw - 1) / fpw;
+    sp.nb = (int)nt;
+    sp.fpw = (int)fpw;
+    sp.waves = o.waves.load() ? o.waves.load() : (ksteps >= 64 ? 8 : 4);
+    int64_t ks = o.ksplit.load() ? o.ksplit.load() : 1;
+    if (ks > ksteps) ks = ksteps;
+    const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
+    ks = (K + kslice - 1) / kslice;
+    sp.ksplit = (int)ks;
+    sp.kslice = (int)kslice;
+    sp.blocks = (int)(groups * ks);
+  } else {
+    sp.nb = o.nb.load() ? o.nb.load() : 1;
+    sp.waves = o.waves.load() ? o.waves.load() : (sp.mt == 8 ? 4 : 8);
+    const int64_t groups = (N + 16 * sp.nb - 1) / (16 * sp.nb);
+    const int64_t target_waves = (int64_t)kCUs * 3;
+    int64_t ks = o.ksplit.load();
+    if (!ks) {
+      ks = (target_waves + groups * sp.waves - 1) / (groups * sp.waves);
+      const int64_t max_ks = ksteps / (2 * (int64_t)sp.waves * sp.u);  // >= two K steps per wave
+      if (ks > max_ks) ks = max_ks;
+      if (ks < 1) ks = 1;
+    }
+    if (ks > ksteps) ks = ksteps;
+    const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
+    ks = (K + kslice - 1) / kslice;
+    sp.ksplit = (int)ks;
+    sp.kslice = (int)kslice;
+    sp.blocks = (int)(groups * ks);
+    sp.fpw = 0;
+  }
+  if (!smlp::skinny_instantiated(stage == 0, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
+  *out = sp;
+  return true;
 }
 
 int out_elem(int dtype, int partial_fp32) { return (dtype == SMLP_FP32 || partial_fp32) ? 4 : 2; }
@@ -114,10 +159,13 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     p->kernels = 2;
   } else if (M < g_threshold.load() && M <= kSmallMaxM) {
     p->path = SMLP_PATH_SMALL_M;
-    p->h_dtype = SMLP_FP32;
+    // h as two bf16 planes (hi + lo): the down kernel is bound by weight bytes, so the
+    // extra activation bytes cost little and h is effectively not rounded.
+    p->h_dtype = SMLP_BF16_HILO;
     p->h_bytes = round_up((size_t)(M * I) * 4, 256);
-    p->gu = plan_skinny(M, I, H);
-    p->dn = plan_skinny(M, H, I);
+    if (!plan_skinny(0, M, I, H, &p->gu) || !plan_skinny(1, M, H, I, &p->dn))
+      return fail(SMLP_ERR_ARG, "the pinned small-M tuning is not a compiled configuration for M = %lld",
+                  (long long)M);
     size_t part = 0;
     if (p->gu.ksplit > 1) part = (size_t)p->gu.ksplit * M * 2 * I * 4;
     if (p->dn.ksplit > 1) {
@@ -128,8 +176,10 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     p->kernels = 2 + (p->gu.ksplit > 1) + (p->dn.ksplit > 1);
   } else {
     p->path = SMLP_PATH_LARGE_M;
-    p->h_dtype = SMLP_BF16;
-    p->h_bytes = round_up((size_t)(M * I) * 2, 256);
+    // one bf16 plane; two (hi + lo) when the down contraction is too short (I < 256)
+    // for the rounding of h to average out
+    p->h_dtype = I < 256 ? SMLP_BF16_HILO : SMLP_BF16;
+    p->h_bytes = round_up((size_t)(M * I) * (p->h_dtype == SMLP_BF16_HILO ? 4 : 2), 256);
     const int64_t tiles_m = (M + 127) / 128;
     p->tgu.bm = 128;
     p->tgu.bn = 64;
@@ -307,6 +357,19 @@ int64_t shared_mlp_set_large_m_threshold(int64_t threshold) {
   }
   ok();
   return g_threshold.exchange(threshold);
+}
+
+int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit) {
+  if (stage < 0 || stage > 1 || kind < 0 || kind > 2 || !(nb == 0 || nb == 1 || nb == 2 || nb == 4) ||
+      !(waves == 0 || waves == 4 || waves == 8) || u < 0 || u > 2 || ksplit < 0 || ksplit > 1024)
+    return fail(SMLP_ERR_ARG, "bad small-M tuning (stage %d kind %d nb %d waves %d u %d ksplit %d)",
+                stage, kind, nb, waves, u, ksplit);
+  g_tune[stage].kind = kind;
+  g_tune[stage].nb = nb;
+  g_tune[stage].waves = waves;
+  g_tune[stage].u = u;
+  g_tune[stage].ksplit = ksplit;
+  return ok();
 }
 
 int shared_mlp_shard_eligible(int flag_on, int use_sequence_parallel, int caller_eligible, int tp,

@@ -48,6 +48,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Buffer resource over [base, base + bytes) for raw buffer loads; a load whose offset
+// is at or past `bytes` returns zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte raw buffer loads: non-temporal (read-once weights) and default policy.
+__device__ __forceinline__ u32x4 buf_ld_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+__device__ __forceinline__ u32x4 buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // 16-byte global loads.  Weights are read exactly once per call, so they are loaded
 // non-temporally; activations are re-read by many workgroups and use normal loads.
 __device__ __forceinline__ u32x4 ld_stream(const void* p) {

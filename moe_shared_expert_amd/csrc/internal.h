@@ -9,13 +9,19 @@ namespace smlp {
 // One weight-streaming (small-M) stage: out-features in blocks of 16, K split into
 // `ksplit` slices over workgroups and into `waves` slices inside a workgroup.
 struct SkinnyPlan {
-  int mt;        // 16-row token tiles (M <= 16 * mt), one of 1, 2, 4, 8
-  int nb;        // 16-feature output blocks per workgroup
+  int kind;      // SKINNY_LDS16 or SKINNY_DIRECT16
+  int mt;        // 16-token tiles (M <= 16 * mt)
+  int nb;        // output tiles per workgroup (SKINNY_LDS16: 16-row MFMA tiles holding
+                 // 8 gate_up features or 16 down rows; SKINNY_DIRECT16: 16-feature blocks)
   int waves;     // waves per workgroup (they split K)
+  int u;         // 64-element K steps per wave per pipeline stage
   int ksplit;    // workgroups along K (1 = no cross-workgroup reduction)
   int kslice;    // K elements per workgroup slice (multiple of 64)
   int blocks;    // total workgroups
+  int fpw;       // SKINNY_LDS16: features (gate_up) or rows (down) per workgroup
 };
+
+enum { SKINNY_LDS16 = 1, SKINNY_DIRECT16 = 2 };
 
 // One stage of the LDS-tiled MFMA path.
 struct TiledPlan {
@@ -38,6 +44,7 @@ struct Plan {
 };
 
 // Weight-streaming stages (skinny.hip).  Return a hipError_t.
+bool skinny_instantiated(bool gate_up, int kind, int mt, int nb, int waves, int u);
 int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
                           hipStream_t s);
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);

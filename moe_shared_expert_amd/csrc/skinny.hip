@@ -3,37 +3,337 @@
 //
 // Shape of the work: C[M, N] = A[M, K] . W[N, K]^T with M small (<= 128) and W large.
 // Every weight byte is used by all M tokens and by nothing else, so the kernels are
-// bound by streaming W from HBM once.  Each wave owns a block of 16 output features
-// (for gate_up: 16 gate rows and the 16 matching up rows) and a slice of K; it loads
-// 16-byte pieces of W straight into registers in the layout the 16x16x32 bf16 MFMA
-// takes as its B operand, loads the matching pieces of A (L2-resident) as the A
-// operand, and accumulates in fp32.  K is split over the waves of a workgroup
-// (reduced through LDS) and optionally over workgroups (reduced by a second,
-// elementwise kernel that also applies the epilogue).
+// bound by streaming W from HBM once.  A wave owns NB blocks of 16 output features
+// (for gate_up: each block is 16 gate rows plus the 16 matching up rows) and a share
+// of K, and accumulates with 16x16x32 bf16 MFMAs in fp32.
+//
+// Memory access: the MFMA operand layout puts 16 different rows in the 16 lanes of
+// each lane group, so loading operands directly in that layout makes every load
+// instruction touch 16 cache lines (64 bytes of each).  Measured on MI355X that
+// caps streaming at ~4-5 TB/s; loading 8 rows x 128 contiguous bytes per instruction
+// (8 full lines) reaches ~6.5 TB/s.  Each wave therefore loads 64-element K steps of
+// its weight rows and activation rows in the 8-row layout, writes them to a
+// wave-private LDS tile (rows padded to 144 bytes, so both the writes and the
+// fragment reads are bank-conflict-light) and reads the MFMA fragments back.  No
+// other wave touches the tile, so no barrier is needed.
+//
+// Loads are software pipelined two stages deep (the next stage's loads are issued
+// before the current stage is written to LDS and multiplied).  The K range of a
+// workgroup is interleaved over its waves in 64-element steps and reduced through
+// LDS in a fixed tree order; a K split over workgroups (for shapes with few feature
+// blocks) is reduced by a second, elementwise kernel that also applies the epilogue.
+//
+// The intermediate h is handed from gate_up to down as two bf16 planes, hi = rne(h)
+// and lo = rne(h - hi), which together carry ~16 significant bits; the down kernel
+// multiplies both (two MFMAs per fragment), so h is effectively not rounded.
 #include "device_common.h"
 #include "internal.h"
 #include "smlp.h"
 
 namespace smlp {
 
+// Kernel modes: the gate_up stage, and the down stage reading h as two bf16 planes.
+enum { MODE_GATE_UP = 0, MODE_DOWN_HILO = 1 };
+
 struct SkArgs {
-  const void* act;     // [M, K]: bf16 (x) or fp32 (h)
-  const uint16_t* w;   // [rows, K] bf16
-  int M, K, N;         // N: output features per row group (I for gate_up, H for down)
-  int up_off;          // gate_up: first row of the up projection (= I)
-  int kslice;          // K elements per workgroup (multiple of 64)
-  void* out;           // ksplit == 1: final output [M, N]
-  float* part;         // ksplit > 1: partial sums [ksplit][M][P*N]
-  int out_f32;         // down: fp32 (1) or bf16 (0) output
+  const uint16_t* a_hi;  // [M, K] bf16 activations (x), or the hi plane of h
+  const uint16_t* a_lo;  // [M, K] lo plane of h (down stage only)
+  const uint16_t* w;     // [rows, K] bf16
+  int M, K, N;           // N: output features per row group (I for gate_up, H for down)
+  int up_off;            // gate_up: first row of the up projection (= I)
+  int kslice;            // K elements per workgroup (multiple of 64)
+  void* out;             // ksplit == 1: gate_up -> h planes, down -> out [M, N]
+  float* part;           // ksplit > 1: partial sums [ksplit][M][P*N]
+  int out_f32;           // down: fp32 (1) or bf16 (0) output
+  int h_planes;          // gate_up (and its finalize): h planes to store, 2 on this path
+  int fpw;               // LDS kernel: features (gate_up) or rows (down) per workgroup
+  int w_rows;            // rows of w
 };
 
-// AF32: activations are fp32 and are fed to the MFMA as bf16 hi + bf16 lo parts
-// (hi = rne(v), lo = rne(v - hi)), which keeps ~16 mantissa bits of h.
-// GU: gate_up stage (two row groups per feature block, SiLU-and-mul epilogue).
-template <int MT, int NB, int WAVES, int U, bool AF32, bool GU>
-__global__ __launch_bounds__(WAVES * 64) void skinny_kernel(SkArgs a) {
+// Store element (m, n) of h: rne(h) in the first plane and, with two planes, the
+// rounding remainder rne(h - hi) in the second.
+__device__ __forceinline__ void store_h(void* base, int M, int N, int m, int n, float h,
+                                        int planes) {
+  const uint32_t hi = f2bf(h);
+  uint16_t* p = reinterpret_cast<uint16_t*>(base);
+  p[(size_t)m * N + n] = (uint16_t)hi;
+  if (planes == 2) p[(size_t)M * N + (size_t)m * N + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
+}
+
+// LDS bytes the cross-wave reduction needs.
+template <int MT, int NB, int WAVES, bool GU>
+constexpr int lds_red_bytes() {
+  return WAVES > 1 ? (WAVES / 2) * (GU ? 2 : 1) * NB * MT * 64 * 16 : 16;
+}
+
+// Reduce the WAVES K-shares of a workgroup as a fixed binary tree through LDS, then
+// let wave 0 write the partial sums (K split) or apply the stage's epilogue.
+// `lds` is a 16-byte aligned buffer of at least lds_red_bytes<...>() bytes.
+template <int MT, int NB, int WAVES, bool GU>
+__device__ __forceinline__ void finish_workgroup(const SkArgs& a,
+                                                 f32x4 (&acc)[GU ? 2 : 1][NB][MT], char* lds) {
   constexpr int P = GU ? 2 : 1;
-  constexpr int AB = AF32 ? 4 : 2;  // bytes per activation element
+  constexpr int NF = P * NB * MT;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  if constexpr (WAVES > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    __syncthreads();
+#pragma unroll
+    for (int half = WAVES / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              red[((wave - half) * NF + (p * NB + nb) * MT + mt) * 64 + lane] = acc[p][nb][mt];
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[p][nb][mt] += red[(wave * NF + (p * NB + nb) * MT + mt) * 64 + lane];
+      }
+      __syncthreads();
+    }
+  }
+  if (wave != 0) return;
+
+  const int ksplit = gridDim.y;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int n = (blockIdx.x * NB + nb) * 16 + ln;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = mt * 16 + lg * 4 + j;
+        if (m >= a.M) continue;
+        if (ksplit > 1) {
+          float* dst = a.part + ((size_t)blockIdx.y * a.M + m) * (size_t)(P * a.N) + n;
+          dst[0] = acc[0][nb][mt][j];
+          if (GU) dst[a.N] = acc[P - 1][nb][mt][j];
+        } else if (GU) {
+          store_h(a.out, a.M, a.N, m, n, silu_mul(acc[0][nb][mt][j], acc[P - 1][nb][mt][j]), a.h_planes);
+        } else if (a.out_f32) {
+          reinterpret_cast<float*>(a.out)[(size_t)m * a.N + n] = acc[0][nb][mt][j];
+        } else {
+          reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.N + n] = (uint16_t)f2bf(acc[0][nb][mt][j]);
+        }
+      }
+    }
+}
+
+// LDS-staged kernel (M <= 32).  A workgroup owns the contiguous feature range
+// [blockIdx.x * fpw, +fpw) and a K slice; the range is cut into NT 16-row MFMA tiles.
+// gate_up tiles pack 8 features: rows 0-7 are their gate rows and rows 8-15 their up
+// rows, so each tile is exactly two 8-row x 128-byte loads; down tiles are 16
+// consecutive rows.  All loads are raw buffer loads: rows past the range, tokens past
+// M and K past the slice get an out-of-range offset, which yields zeros and moves no
+// bytes, so the loop has no branches and no separate tail.
+template <int MT, int NT, int WAVES, int MODE>
+__global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
+  constexpr bool GU = MODE == MODE_GATE_UP;
+  constexpr int NA = GU ? 1 : 2;                      // activation planes: x, or h hi + lo
+  constexpr int TA = NA * MT;                         // activation tiles per K step
+  constexpr int TT = NT + TA;
+  constexpr int ROWB = 144;                           // padded LDS row: 128 data bytes + 16
+  constexpr int TILEB = 16 * ROWB;
+  constexpr int STAGE_LDS = WAVES * TT * TILEB;
+  constexpr int RED_LDS = lds_red_bytes<MT, NT, WAVES, false>();
+  __shared__ __attribute__((aligned(16))) char lds[STAGE_LDS > RED_LDS ? STAGE_LDS : RED_LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;  // 8-row load layout: row, 16-byte chunk
+  const int K = a.K;
+  char* my = lds + wave * (TT * TILEB);
+
+  const int f0 = blockIdx.x * a.fpw;
+  const int fend = min(a.N, f0 + a.fpw);
+  const uint32_t wbytes = (uint32_t)a.w_rows * (uint32_t)K * 2u;
+  const uint32_t abytes = (uint32_t)a.M * (uint32_t)K * 2u;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, wbytes);
+  const __amdgpu_buffer_rsrc_t ar[2] = {make_rsrc(a.a_hi, abytes), make_rsrc(NA == 2 ? a.a_lo : a.a_hi, abytes)};
+
+  // Per-lane row byte offsets (chunk included) or the out-of-range marker.
+  uint32_t wo[NT][2], ao[TA][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int row;
+      bool ok;
+      if (GU) {
+        const int f = f0 + 8 * t + lr;
+        ok = f < fend;
+        row = h ? a.up_off + f : f;
+      } else {
+        row = f0 + 16 * t + 8 * h + lr;
+        ok = row < fend;
+      }
+      wo[t][h] = ok ? (uint32_t)row * (uint32_t)K * 2u + lc * 16 : wbytes;
+    }
+#pragma unroll
+  for (int q = 0; q < NA; ++q)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = mt * 16 + 8 * h + lr;
+        ao[q * MT + mt][h] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + lc * 16 : abytes;
+      }
+
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kbeg = blockIdx.y * a.kslice;
+  const int kend = min(K, kbeg + a.kslice);
+  constexpr int STEP = 64 * WAVES;
+  const int nst = (kend - kbeg + STEP - 1) / STEP;
+
+  struct Stage {
+    u32x4 w[NT][2];
+    u32x4 x[TA][2];
+  };
+  auto load = [&](Stage& s, int i) {
+    const int k = kbeg + (i * WAVES + wave) * 64;
+    const bool kok = k + lc * 8 < kend;
+    const uint32_t kb = (uint32_t)k * 2u;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s.w[t][h] = buf_ld_nt(wr, (kok && wo[t][h] != wbytes) ? wo[t][h] + kb : wbytes);
+#pragma unroll
+    for (int t = 0; t < TA; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s.x[t][h] = buf_ld(ar[t / MT], (kok && ao[t][h] != abytes) ? ao[t][h] + kb : abytes);
+  };
+  auto compute = [&](const Stage& s) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(my + t * TILEB + (8 * h + lr) * ROWB + lc * 16) = s.w[t][h];
+#pragma unroll
+    for (int t = 0; t < TA; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(my + (NT + t) * TILEB + (8 * h + lr) * ROWB + lc * 16) = s.x[t][h];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int foff = ln * ROWB + (4 * j + lg) * 16;
+      u32x4 fb[NT], fa[TA];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) fb[t] = *reinterpret_cast<const u32x4*>(my + t * TILEB + foff);
+#pragma unroll
+      for (int t = 0; t < TA; ++t) fa[t] = *reinterpret_cast<const u32x4*>(my + (NT + t) * TILEB + foff);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16x16x32(fa[q * MT + mt], fb[t], acc[t][mt]);
+    }
+  };
+
+  // Two-stage software pipeline, unrolled by two so that the stage buffers alternate
+  // without register copies.  Stages past the slice load zeros (no memory traffic),
+  // so the trip count is rounded up to even without a branch.  sched_barrier keeps
+  // every load of the next stage issued before the current stage is consumed.
+  Stage s0, s1;
+  load(s0, 0);
+  for (int i = 0; i < nst; i += 2) {
+    load(s1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(s0, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Reduce the WAVES K-shares of the workgroup through LDS (reusing the staging
+  // tiles), as a fixed binary tree.
+  if constexpr (WAVES > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    __syncthreads();
+#pragma unroll
+    for (int half = WAVES / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) red[((wave - half) * NT * MT + t * MT + mt) * 64 + lane] = acc[t][mt];
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] += red[(wave * NT * MT + t * MT + mt) * 64 + lane];
+      }
+      __syncthreads();
+    }
+  }
+  if (wave != 0) return;
+
+  // Epilogue.  MFMA output: lane (ln, lg), element j = (token mt*16 + 4*lg + j, column ln).
+  const int ksplit = gridDim.y;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = mt * 16 + lg * 4 + j;
+        const float v = acc[t][mt][j];
+        if (GU) {
+          const float up = __shfl_xor(v, 8, 64);  // column ln ^ 8 of the same row
+          const int f = f0 + 8 * t + (ln & 7);
+          if (m >= a.M || f >= fend) continue;
+          if (ksplit > 1) {
+            // lanes 0-7 hold gate columns, lanes 8-15 the matching up columns
+            a.part[((size_t)blockIdx.y * a.M + m) * (size_t)(2 * a.N) + (ln < 8 ? f : a.N + f)] = v;
+          } else if (ln < 8) {
+            store_h(a.out, a.M, a.N, m, f, silu_mul(v, up), a.h_planes);
+          }
+        } else {
+          const int n = f0 + 16 * t + ln;
+          if (m >= a.M || n >= fend) continue;
+          if (ksplit > 1)
+            a.part[((size_t)blockIdx.y * a.M + m) * (size_t)a.N + n] = v;
+          else if (a.out_f32)
+            reinterpret_cast<float*>(a.out)[(size_t)m * a.N + n] = v;
+          else
+            reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.N + n] = (uint16_t)f2bf(v);
+        }
+      }
+}
+
+// Direct-load variant for larger token tiles (MT >= 4), where staging every
+// activation tile through LDS per wave would not fit: operands are loaded straight
+// into registers in the MFMA layout.
+template <int MT, int NB, int WAVES, int U, int MODE>
+__global__ __launch_bounds__(WAVES * 64) void skinny_direct_kernel(SkArgs a) {
+  constexpr bool GU = MODE == MODE_GATE_UP;
+  constexpr int P = GU ? 2 : 1;                      // row groups per feature block
+  constexpr int NA = GU ? 1 : 2;                      // activation planes: x, or h hi + lo
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
@@ -46,16 +346,18 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(SkArgs a) {
     n = n < a.N ? n : a.N - 1;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      int row = p ? a.up_off + n : n;
+      const int row = p ? a.up_off + n : n;
       wrow[p][nb] = reinterpret_cast<const char*>(a.w) + ((size_t)row * K + lg * 8) * 2;
     }
   }
-  const char* arow[MT];
+  const char* arow[NA][MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     int m = mt * 16 + ln;
     m = m < a.M ? m : a.M - 1;
-    arow[mt] = reinterpret_cast<const char*>(a.act) + ((size_t)m * K + lg * 8) * AB;
+#pragma unroll
+    for (int q = 0; q < NA; ++q)
+      arow[q][mt] = reinterpret_cast<const char*>(q ? a.a_lo : a.a_hi) + ((size_t)m * K + lg * 8) * 2;
   }
 
   f32x4 acc[P][NB][MT];
@@ -70,132 +372,112 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(SkArgs a) {
   const int kend = min(K, kbeg + a.kslice);
   constexpr int STEP = 64 * WAVES * U;
 
-  for (int kit = kbeg; kit < kend; kit += STEP) {
-    u32x4 bw[U][2][P][NB];
-    u32x4 av[U][2][MT][AF32 ? 2 : 1];
+  struct Stage {
+    u32x4 w[U][2][P][NB];
+    u32x4 x[U][2][NA][MT];
+  };
+  auto load = [&](Stage& s, int kit) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int koff = kit + (u * WAVES + wave) * 64 + j * 32;  // + lg*8 folded in pointers
-        const bool valid = koff + lg * 8 < kend;
+        const size_t off = (size_t)(kit + (u * WAVES + wave) * 64 + j * 32) * 2;
 #pragma unroll
         for (int p = 0; p < P; ++p)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            bw[u][j][p][nb] = valid ? ld_stream(wrow[p][nb] + (size_t)koff * 2) : u32x4{0, 0, 0, 0};
+          for (int nb = 0; nb < NB; ++nb) s.w[u][j][p][nb] = ld_stream(wrow[p][nb] + off);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (AF32) {
-            av[u][j][mt][0] = valid ? ld16(arow[mt] + (size_t)koff * 4) : u32x4{0, 0, 0, 0};
-            av[u][j][mt][AF32 ? 1 : 0] =
-                valid ? ld16(arow[mt] + (size_t)koff * 4 + 16) : u32x4{0, 0, 0, 0};
-          } else {
-            av[u][j][mt][0] = valid ? ld16(arow[mt] + (size_t)koff * 2) : u32x4{0, 0, 0, 0};
-          }
-        }
+        for (int q = 0; q < NA; ++q)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) s.x[u][j][q][mt] = ld16(arow[q][mt] + off);
       }
+  };
+  auto load_masked = [&](Stage& s, int kit) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int koff = kit + (u * WAVES + wave) * 64 + j * 32;
+        const bool valid = koff + lg * 8 < kend;
+        const size_t off = valid ? (size_t)koff * 2 : 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 v = ld_stream(wrow[p][nb] + off);
+            s.w[u][j][p][nb] = valid ? v : u32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const u32x4 v = ld16(arow[q][mt] + off);
+            s.x[u][j][q][mt] = valid ? v : u32x4{0, 0, 0, 0};
+          }
+      }
+  };
+  auto compute = [&](const Stage& s) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          u32x4 ahi, alo;
-          if (AF32) {
-            const u32x4 v0 = av[u][j][mt][0], v1 = av[u][j][mt][AF32 ? 1 : 0];
-            float f[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
-                          __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
-                          __uint_as_float(v1.z), __uint_as_float(v1.w)};
-            uint32_t hb[8], lb[8];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              hb[e] = f2bf(f[e]);
-              lb[e] = f2bf(f[e] - __uint_as_float(hb[e] << 16));
-            }
-            ahi = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                        hb[6] | (hb[7] << 16)};
-            alo = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                        lb[6] | (lb[7] << 16)};
-          } else {
-            ahi = av[u][j][mt][0];
-          }
+          for (int q = 0; q < NA; ++q)
 #pragma unroll
-          for (int p = 0; p < P; ++p)
+            for (int p = 0; p < P; ++p)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              acc[p][nb][mt] = mfma16x16x32(ahi, bw[u][j][p][nb], acc[p][nb][mt]);
-              if (AF32) acc[p][nb][mt] = mfma16x16x32(alo, bw[u][j][p][nb], acc[p][nb][mt]);
-            }
-        }
-  }
+              for (int nb = 0; nb < NB; ++nb)
+                acc[p][nb][mt] = mfma16x16x32(s.x[u][j][q][mt], s.w[u][j][p][nb], acc[p][nb][mt]);
+  };
 
-  // Reduce the WAVES K-slices of the workgroup through LDS, in wave order.
-  constexpr int NF = P * NB * MT;
-  if constexpr (WAVES > 1) {
-    __shared__ f32x4 red[WAVES][NF][64];
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[wave][(p * NB + nb) * MT + mt][lane] = acc[p][nb][mt];
-    __syncthreads();
-    // Output unit q = (nb, mt) is finished by wave q % WAVES.
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (((nb * MT + mt) % WAVES) != wave) continue;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          f32x4 s = red[0][(p * NB + nb) * MT + mt][lane];
-#pragma unroll
-          for (int w = 1; w < WAVES; ++w) s += red[w][(p * NB + nb) * MT + mt][lane];
-          acc[p][nb][mt] = s;
-        }
-      }
-  }
-
-  const int ksplit = gridDim.y;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (WAVES > 1 && ((nb * MT + mt) % WAVES) != wave) continue;
-      const int n = (blockIdx.x * NB + nb) * 16 + ln;
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = mt * 16 + lg * 4 + j;
-        if (m >= a.M) continue;
-        if (ksplit > 1) {
-          float* dst = a.part + ((size_t)blockIdx.y * a.M + m) * (size_t)(P * a.N) + n;
-          dst[0] = acc[0][nb][mt][j];
-          if (GU) dst[a.N] = acc[P - 1][nb][mt][j];
-        } else if (GU) {
-          reinterpret_cast<float*>(a.out)[(size_t)m * a.N + n] =
-              silu_mul(acc[0][nb][mt][j], acc[P - 1][nb][mt][j]);
-        } else if (a.out_f32) {
-          reinterpret_cast<float*>(a.out)[(size_t)m * a.N + n] = acc[0][nb][mt][j];
-        } else {
-          reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.N + n] =
-              (uint16_t)f2bf(acc[0][nb][mt][j]);
-        }
-      }
+  const int nfull = (kend - kbeg) / STEP;
+  Stage s0, s1;
+  int kit = kbeg;
+  if (nfull > 0) {
+    load(s0, kit);
+    int i = 0;
+    for (; i + 2 < nfull; i += 2) {
+      load(s1, kit + STEP);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(s0, kit + 2 * STEP);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s1);
+      __builtin_amdgcn_sched_barrier(0);
+      kit += 2 * STEP;
     }
+    if (i + 1 < nfull) {
+      load(s1, kit + STEP);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s0);
+      compute(s1);
+      kit += 2 * STEP;
+    } else {
+      compute(s0);
+      kit += STEP;
+    }
+  }
+  if (kit < kend) {
+    load_masked(s0, kit);
+    compute(s0);
+  }
+  __shared__ __attribute__((aligned(16))) char red[lds_red_bytes<MT, NB, WAVES, GU>()];
+  finish_workgroup<MT, NB, WAVES, GU>(a, acc, red);
 }
 
 // Sum the ksplit partials in slice order and apply the stage's epilogue.
 template <bool GU>
 __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__ part,
                                                        int ksplit, int M, int N, void* out,
-                                                       int out_f32) {
+                                                       int out_f32, int h_planes) {
   const int P = GU ? 2 : 1;
   const size_t total = (size_t)M * N;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
-    const size_t m = e / N, n = e % N;
+    const int m = (int)(e / N), n = (int)(e % N);
     float g = 0.f, u = 0.f;
     for (int s = 0; s < ksplit; ++s) {
       const float* src = part + ((size_t)s * M + m) * (size_t)(P * N) + n;
@@ -203,7 +485,7 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
       if (GU) u += src[N];
     }
     if (GU)
-      reinterpret_cast<float*>(out)[e] = silu_mul(g, u);
+      store_h(out, M, N, m, n, silu_mul(g, u), h_planes);
     else if (out_f32)
       reinterpret_cast<float*>(out)[e] = g;
     else
@@ -211,39 +493,78 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
   }
 }
 
-template <bool AF32, bool GU>
+// Instantiated configurations (MT, NB, WAVES, U) per kernel kind (MT = 16-token
+// tiles, NB = 16-feature blocks); none spills registers.
+#define SMLP_SK_LDS16(X)                                                                       \
+  X(1, 1, 4, 1) X(1, 1, 8, 1) X(1, 2, 4, 1) X(1, 2, 8, 1) X(1, 3, 4, 1) X(1, 3, 8, 1)          \
+  X(1, 4, 4, 1) X(1, 4, 8, 1) X(2, 1, 4, 1) X(2, 1, 8, 1) X(2, 2, 4, 1) X(2, 2, 8, 1)          \
+  X(2, 3, 4, 1) X(2, 3, 8, 1) X(2, 4, 4, 1)
+#define SMLP_SK_GU_LDS16(X) SMLP_SK_LDS16(X)
+#define SMLP_SK_DN_LDS16(X) SMLP_SK_LDS16(X)
+#define SMLP_SK_GU_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1) X(8, 1, 8, 1)
+#define SMLP_SK_DN_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1)
+bool skinny_instantiated(bool gu, int kind, int mt, int nb, int waves, int u) {
+#define SMLP_MATCH(MT_, NB_, W_, U_) \
+  if (mt == MT_ && nb == NB_ && waves == W_ && u == U_) return true;
+  if (gu) {
+    if (kind == SKINNY_LDS16) { SMLP_SK_GU_LDS16(SMLP_MATCH) }
+    if (kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_MATCH) }
+  } else {
+    if (kind == SKINNY_LDS16) { SMLP_SK_DN_LDS16(SMLP_MATCH) }
+    if (kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_MATCH) }
+  }
+#undef SMLP_MATCH
+  return false;
+}
+
+template <int MODE>
 static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
+  constexpr bool GU = MODE == MODE_GATE_UP;
   dim3 grid(sp.blocks / sp.ksplit, sp.ksplit);
   dim3 block(sp.waves * 64);
-#define SMLP_SK(MT_, NB_, U_)                                                             \
-  if (sp.mt == MT_ && sp.nb == NB_ && sp.waves == 4) {                                   \
-    hipLaunchKernelGGL((skinny_kernel<MT_, NB_, 4, U_, AF32, GU>), grid, block, 0, s, a); \
+#define SMLP_SK(KERNEL)                                                                  \
+  if (sp.mt == MT_ && sp.nb == NB_ && sp.waves == W_ && sp.u == U_) {                    \
+    hipLaunchKernelGGL((KERNEL<MT_, NB_, W_, U_, MODE>), grid, block, 0, s, a);          \
     return (int)hipGetLastError();                                                       \
   }
-  SMLP_SK(1, 1, 2) SMLP_SK(2, 1, 2) SMLP_SK(4, 1, 1) SMLP_SK(8, 1, 1)
-  SMLP_SK(1, 2, 2) SMLP_SK(2, 2, 2) SMLP_SK(4, 2, 1) SMLP_SK(8, 2, 1)
+#define SMLP_SK_L(MT__, NB__, W__, U__)                                                  \
+  if (sp.mt == MT__ && sp.nb == NB__ && sp.waves == W__ && sp.u == U__) {                \
+    hipLaunchKernelGGL((skinny_lds_kernel<MT__, NB__, W__, MODE>), grid, block, 0, s, a); \
+    return (int)hipGetLastError();                                                       \
+  }
+#define SMLP_SK_D(MT__, NB__, W__, U__) { constexpr int MT_ = MT__, NB_ = NB__, W_ = W__, U_ = U__; SMLP_SK(skinny_direct_kernel) }
+  if constexpr (GU) {
+    if (sp.kind == SKINNY_LDS16) { SMLP_SK_GU_LDS16(SMLP_SK_L) }
+    if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_SK_D) }
+  } else {
+    if (sp.kind == SKINNY_LDS16) { SMLP_SK_DN_LDS16(SMLP_SK_L) }
+    if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_SK_D) }
+  }
+#undef SMLP_SK_L
+#undef SMLP_SK_D
 #undef SMLP_SK
   return (int)hipErrorInvalidConfiguration;
 }
 
 static int finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int out_f32,
-                    hipStream_t s) {
+                    int h_planes, hipStream_t s) {
   const size_t total = (size_t)M * N;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   if (gu)
     hipLaunchKernelGGL(skinny_finalize<true>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
-                       out, out_f32);
+                       out, out_f32, h_planes);
   else
     hipLaunchKernelGGL(skinny_finalize<false>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
-                       out, out_f32);
+                       out, out_f32, h_planes);
   return (int)hipGetLastError();
 }
 
 int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
                           hipStream_t s) {
   SkArgs a;
-  a.act = x;
+  a.a_hi = reinterpret_cast<const uint16_t*>(x);
+  a.a_lo = nullptr;
   a.w = reinterpret_cast<const uint16_t*>(w_gate_up);
   a.M = (int)p.M;
   a.K = (int)p.H;
@@ -252,15 +573,20 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.kslice = p.gu.kslice;
   a.out = static_cast<char*>(ws) + p.h_offset;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
-  a.out_f32 = 1;
-  int rc = launch_stage<false, true>(p.gu, a, s);
+  a.out_f32 = 0;
+  a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
+  a.fpw = p.gu.fpw;
+  a.w_rows = (int)(2 * p.I);
+  int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
   if (rc || p.gu.ksplit == 1) return rc;
-  return finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, 1, s);
+  return finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, 0, a.h_planes, s);
 }
 
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
   SkArgs a;
-  a.act = static_cast<const char*>(ws) + p.h_offset;
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.h_offset);
+  a.a_hi = h;
+  a.a_lo = p.h_dtype == SMLP_BF16_HILO ? h + (size_t)p.M * p.I : nullptr;
   a.w = reinterpret_cast<const uint16_t*>(w_down);
   a.M = (int)p.M;
   a.K = (int)p.I;
@@ -270,9 +596,12 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.out = out;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = p.partial_fp32 ? 1 : 0;
-  int rc = launch_stage<true, false>(p.dn, a, s);
+  a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
+  a.fpw = p.dn.fpw;
+  a.w_rows = (int)p.H;
+  int rc = launch_stage<MODE_DOWN_HILO>(p.dn, a, s);
   if (rc || p.dn.ksplit == 1) return rc;
-  return finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.out_f32, s);
+  return finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.out_f32, 1, s);
 }
 
 }  // namespace smlp

@@ -26,18 +26,46 @@ def L():
     return binding.lib()
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "smlp.h")).read()
+def _declared(header):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(shared_mlp_\w+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(L):
-    names = _declared()
+    names = _declared("smlp.h")
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTS), "binding and header disagree"
+    tuning = _declared("smlp_tuning.h")
+    for n in tuning:
+        assert hasattr(L, n), n
+    assert set(tuning) == set(binding.TUNING_EXPORTS)
+
+
+def test_tuning_hook(L):
+    try:
+        binding.shared_mlp_tune_skinny(0, kind=1, nb=2, waves=8, u=1, ksplit=3)
+        p = binding.shared_mlp_plan(16, H, I)
+        assert p["gate_up_ksplit"] == 3 and p["gate_up_blocks"] == 3 * (I // 16)
+        binding.shared_mlp_tune_skinny(0)
+        p = binding.shared_mlp_plan(16, H, I)
+        assert p["gate_up_ksplit"] == 1 and p["gate_up_blocks"] == 256
+        binding.shared_mlp_tune_skinny(0, kind=2, nb=1, waves=4, u=1, ksplit=2)
+        p = binding.shared_mlp_plan(64, H, I)
+        assert p["gate_up_ksplit"] == 2 and p["gate_up_blocks"] == 2 * (I // 16)
+        binding.shared_mlp_tune_skinny(0, kind=1, nb=1, waves=4, u=1, ksplit=1)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_plan(64, H, I)   # the LDS-staged kind serves M <= 32 only
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_skinny(0, nb=3)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_skinny(0, kind=3)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_skinny(2)
+    finally:
+        binding.shared_mlp_tune_skinny(0)
 
 
 def test_status_strings(L):
@@ -108,7 +136,8 @@ def test_stage_entry_points_validate(L):
 
 def test_workspace_and_plan(L):
     p = binding.shared_mlp_plan(16, H, I)
-    assert p["path_name"] == "small_m" and p["h_dtype"] == FP32
+    assert p["path_name"] == "small_m" and p["h_dtype"] == binding.SMLP_BF16_HILO
+    assert binding.shared_mlp_plan(8192, H, 128)["h_dtype"] == binding.SMLP_BF16_HILO
     assert p["workspace_bytes"] >= 16 * I * 4
     p = binding.shared_mlp_plan(8192, H, I)
     assert p["path_name"] == "large_m" and p["h_dtype"] == BF16

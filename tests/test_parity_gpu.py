@@ -318,9 +318,13 @@ def test_stage_entry_points(M):
     ws = workspace_for(M, Hh, Ii, binding.SMLP_BF16)
     binding.shared_mlp_gate_up_act(xd, gd, ws)
     torch.cuda.synchronize()
-    h = binding.read_h(ws, M, Ii, Hh).clone()
+    h = f64(binding.read_h(ws, M, Ii, Hh).clone())
     h_ref = oracle.gate_up_act(f64(x), f64(wgu))
-    assert_rms_close(h, h_ref, BF16_TOL, f"stage gate_up_act M={M}")
+    # h is an intermediate, stored as one bf16 plane or two (hi + lo): elementwise it is
+    # the exact value rounded at most once to bf16 (relative 2^-9), plus fp32
+    # accumulation error of the two contractions (bounded here by 2e-3 * RMS).
+    bound = 2.0 ** -8 * np.abs(h_ref) + 2e-3 * rms(h_ref)
+    assert np.all(np.abs(h - h_ref) <= bound), f"stage gate_up_act M={M}"
     out = torch.empty(M, Hh, dtype=torch.bfloat16, device=DEV)
     binding.shared_mlp_down(dd, out, ws)
     torch.cuda.synchronize()
