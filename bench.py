@@ -129,6 +129,30 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
     }
 
 
+KERNEL_SOURCES = ("moe_shared_expert_amd/csrc/skinny.hip", "moe_shared_expert_amd/csrc/tiled.hip",
+                  "moe_shared_expert_amd/csrc/device_common.h", "moe_shared_expert_amd/csrc/api.cpp")
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch of the gate_up kernel from the committed rocprofv3 counter
+    summary of this workload (profiles/<workload>.md), or None when that summary was
+    taken on different kernel sources than the ones built now."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    m = re.search(r"kernel source hash[^`]*`([0-9a-f]+)`", text)
+    t = re.search(r"gate_up traffic bytes per launch: (\d+)", text)
+    if not m or not t or m.group(1) != h.hexdigest()[:16]:
+        return None
+    return int(t.group(1))
+
+
 def cpu_baseline(name, budget_s=12.0):
     """The fp64 oracle on host cores, on a bounded sample of the same workload."""
     import numpy as np
@@ -171,12 +195,24 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also print the M sweep lines")
     ap.add_argument("--launch", default="graph", choices=("graph", "eager"),
                     help="replay the steps from a captured hipGraph (default) or launch eagerly")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 3 device copies of 256 MiB (the reference kernel for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path "
                                    "(all-gather / reduce-scatter over RCCL) is not built"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 3}))
+        return
     binding.lib()
     r = run_workload(args.workload, args.steps, args.warmup, dev, args.launch)
     line = {
@@ -196,7 +232,8 @@ def main():
                      "achieved": round(r["gate_up_gbs"], 1), "peak": roofline.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["gate_up_gbs"] / roofline.HBM_PEAK_GBS, 4),
                      "kernel_us": round(r["gate_up_us"], 3),
-                     "bytes_per_launch": r["gate_up_alg_bytes"], "traffic": None},
+                     "bytes_per_launch": r["gate_up_alg_bytes"],
+                     "traffic": profiled_traffic(args.workload)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
