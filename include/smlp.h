@@ -132,10 +132,12 @@ int shared_mlp_down(const void* w_down, void* out, int64_t M, int64_t H, int64_t
 
 /*
  * M-dispatch threshold: bf16 calls with M >= threshold take the LDS-tiled MFMA path,
- * smaller M the weight-streaming path.  The initial value is 256, or the value of
- * the environment variable SMLP_LARGE_M_MIN read at library load.  Returns the
- * previous threshold, or -1 (SMLP_ERR_ARG detail) if threshold < 1.  Process-wide;
- * not synchronised with calls in flight on other threads.
+ * smaller M the weight-streaming path (which serves at most 128 tokens, so M > 128
+ * always takes the tiled path).  The initial value is 33, or the value of the
+ * environment variable SMLP_LARGE_M_MIN (an integer in [1, 129]) read at library
+ * load.  Returns the previous threshold, or -1 (SMLP_ERR_ARG detail) if threshold is
+ * outside [1, 129].  Process-wide; not synchronised with calls in flight on other
+ * threads.
  */
 int64_t shared_mlp_set_large_m_threshold(int64_t threshold);
 

@@ -21,6 +21,9 @@ thread_local std::string g_last_error;
 constexpr int kCUs = 256;
 // The weight-streaming kernels handle up to 128 tokens per call.
 constexpr int64_t kSmallMaxM = 128;
+// Default M-dispatch threshold: on MI355X the LDS-staged weight-streaming kernel is
+// fastest up to 32 tokens and the LDS-tiled path from 33 on.
+constexpr int64_t kDefaultLargeMMin = 33;
 constexpr int64_t kLimit = (int64_t)1 << 31;
 
 int64_t initial_threshold() {
@@ -30,7 +33,7 @@ int64_t initial_threshold() {
     long long v = std::strtoll(e, &end, 10);
     if (end && *end == '\0' && v >= 1 && v <= kSmallMaxM + 1) return (int64_t)v;
   }
-  return kSmallMaxM + 1;
+  return kDefaultLargeMMin;
 }
 std::atomic<int64_t> g_threshold{initial_threshold()};
 
@@ -64,6 +67,11 @@ struct SkinnyOverride {
   std::atomic<int> kind{0}, nb{0}, waves{0}, u{0}, ksplit{0};
 };
 SkinnyOverride g_tune[2];
+
+struct GemmOverride {
+  std::atomic<int> bm{0}, bn{0}, wm{0}, wn{0}, ns{0}, ksplit{0};
+};
+GemmOverride g_gtune[2];
 
 // Small-M stage plan.  M <= 32: the LDS-staged kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
@@ -126,6 +134,71 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
   return true;
 }
 
+// LDS-tiled GEMM stage plan (measured on MI355X over M = 64 .. 8192, I = 768 and 6144):
+// 256 x 256 tiles (8 waves, 128 x 64 per wave) when they fill the chip at least twice
+// over and K is long; otherwise 128 x 128 tiles (4 waves) for gate_up unless there are
+// very few of them, and for down when they fill the chip twice; else 128 x 64 tiles.
+// Two LDS stages, so that two workgroups share a compute unit, and a K split over
+// workgroups when the tiles alone leave compute units idle.  N counts gate_up features
+// (two weight rows each) or down rows.  Returns false if a pinned tile is not compiled.
+bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::GemmPlan* out) {
+  smlp::GemmPlan gp{};
+  const GemmOverride& o = g_gtune[stage];
+  const int64_t fpr = stage == 0 ? 2 : 1;  // weight rows per output feature
+  auto tiles_for = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N * fpr + bn - 1) / bn); };
+  if (o.bm.load() && o.bn.load()) {
+    gp.bm = o.bm.load();
+    gp.bn = o.bn.load();
+  } else if (!hilo && tiles_for(256, 256) >= 2 * kCUs && K >= 4096) {
+    gp.bm = 256;
+    gp.bn = 256;
+  } else if (tiles_for(128, 128) >= (stage == 0 ? 64 : 2 * kCUs)) {
+    gp.bm = 128;
+    gp.bn = 128;
+  } else {
+    gp.bm = 128;
+    gp.bn = 64;
+  }
+  if (o.wm.load() && o.wn.load()) {
+    gp.wm = o.wm.load();
+    gp.wn = o.wn.load();
+  } else if (gp.bm == 256) {
+    gp.wm = 2;
+    gp.wn = 4;
+  } else if (gp.bn == 64) {
+    gp.wm = 4;
+    gp.wn = 1;
+  } else {
+    gp.wm = 2;
+    gp.wn = 2;
+  }
+  if (o.ns.load()) {
+    gp.ns = o.ns.load();
+  } else {
+    // Two stages where compiled (the two-plane 128 x 128 down tile has three).
+    gp.ns = 2;
+    while (gp.ns < 4 && !smlp::gemm_instantiated(hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) ++gp.ns;
+  }
+  if (!smlp::gemm_instantiated(hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) return false;
+  gp.tiles_m = (int)((M + gp.bm - 1) / gp.bm);
+  const int64_t tiles = tiles_for(gp.bm, gp.bn);
+  gp.tiles = (int)tiles;
+  const int64_t ksteps = (K + 63) / 64;
+  int64_t ks = o.ksplit.load();
+  if (!ks) {
+    ks = tiles >= kCUs ? 1 : (kCUs + tiles - 1) / tiles;
+    const int64_t max_ks = ksteps / 2;  // at least two 64-element K steps per slice
+    if (ks > max_ks) ks = max_ks;
+    if (ks < 1) ks = 1;
+  }
+  if (ks > ksteps) ks = ksteps;
+  const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
+  gp.ksplit = (int)((K + kslice - 1) / kslice);
+  gp.kslice = (int)kslice;
+  *out = gp;
+  return true;
+}
+
 int out_elem(int dtype, int partial_fp32) { return (dtype == SMLP_FP32 || partial_fp32) ? 4 : 2; }
 
 // Shape/dtype validation and plan; no pointer checks.
@@ -180,14 +253,18 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     // for the rounding of h to average out
     p->h_dtype = I < 256 ? SMLP_BF16_HILO : SMLP_BF16;
     p->h_bytes = round_up((size_t)(M * I) * (p->h_dtype == SMLP_BF16_HILO ? 4 : 2), 256);
-    const int64_t tiles_m = (M + 127) / 128;
-    p->tgu.bm = 128;
-    p->tgu.bn = 64;
-    p->tgu.blocks = (int)(tiles_m * ((I + 63) / 64));
-    p->tdn.bm = 128;
-    p->tdn.bn = 128;
-    p->tdn.blocks = (int)(tiles_m * ((H + 127) / 128));
-    p->kernels = 2;
+    const bool hilo = p->h_dtype == SMLP_BF16_HILO;
+    // Only the down stage reads h; its two-plane form has its own tile list.
+    if (!plan_gemm(0, M, I, H, false, &p->ggu) || !plan_gemm(1, M, H, I, hilo, &p->gdn))
+      return fail(SMLP_ERR_ARG, "the pinned large-M tile is not a compiled configuration");
+    size_t part = 0;
+    if (p->ggu.ksplit > 1) part = (size_t)p->ggu.ksplit * M * 2 * I * 4;
+    if (p->gdn.ksplit > 1) {
+      const size_t d = (size_t)p->gdn.ksplit * M * H * 4;
+      if (d > part) part = d;
+    }
+    p->part_bytes = round_up(part, 256);
+    p->kernels = 2 + (p->ggu.ksplit > 1) + (p->gdn.ksplit > 1);
   }
   p->h_offset = 0;
   p->part_offset = p->h_bytes;
@@ -250,7 +327,7 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
         rc = smlp::launch_fp32_gate_up(p, (const float*)x, (const float*)wgu, ws, stream);
         break;
       case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_gate_up(p, x, wgu, ws, stream); break;
-      default: rc = smlp::launch_tiled_gate_up(p, x, wgu, ws, stream); break;
+      default: rc = smlp::launch_gemm_gate_up(p, x, wgu, ws, stream); break;
     }
     if ((rc = hip_status(rc, "gate_up launch"))) return rc;
   }
@@ -260,7 +337,7 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
         rc = smlp::launch_fp32_down(p, (const float*)wd, (float*)out, ws, stream);
         break;
       case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_down(p, wd, out, ws, stream); break;
-      default: rc = smlp::launch_tiled_down(p, wd, out, ws, stream); break;
+      default: rc = smlp::launch_gemm_down(p, wd, out, ws, stream); break;
     }
     if ((rc = hip_status(rc, "down launch"))) return rc;
   }
@@ -304,9 +381,10 @@ int shared_mlp_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32
     plan->gate_up_blocks = p.gu.blocks;
     plan->down_blocks = p.dn.blocks;
   } else if (p.path == SMLP_PATH_LARGE_M) {
-    plan->gate_up_ksplit = plan->down_ksplit = 1;
-    plan->gate_up_blocks = p.tgu.blocks;
-    plan->down_blocks = p.tdn.blocks;
+    plan->gate_up_ksplit = p.ggu.ksplit;
+    plan->down_ksplit = p.gdn.ksplit;
+    plan->gate_up_blocks = p.ggu.tiles * p.ggu.ksplit;
+    plan->down_blocks = p.gdn.tiles * p.gdn.ksplit;
   } else {
     plan->gate_up_ksplit = plan->down_ksplit = 1;
     plan->gate_up_blocks = plan->down_blocks = 0;
@@ -369,6 +447,22 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
   g_tune[stage].waves = waves;
   g_tune[stage].u = u;
   g_tune[stage].ksplit = ksplit;
+  return ok();
+}
+
+int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit) {
+  if (stage < 0 || stage > 1 || !(bm == 0 || bm == 128 || bm == 256) ||
+      !(bn == 0 || bn == 64 || bn == 128 || bn == 256) || (bm == 0) != (bn == 0) ||
+      !(wm == 0 || wm == 1 || wm == 2 || wm == 4) || !(wn == 0 || wn == 1 || wn == 2 || wn == 4) ||
+      (wm == 0) != (wn == 0) || ns < 0 || ns > 8 || ksplit < 0 || ksplit > 1024)
+    return fail(SMLP_ERR_ARG, "bad large-M tuning (stage %d bm %d bn %d wm %d wn %d ns %d ksplit %d)", stage,
+                bm, bn, wm, wn, ns, ksplit);
+  g_gtune[stage].bm = bm;
+  g_gtune[stage].bn = bn;
+  g_gtune[stage].wm = wm;
+  g_gtune[stage].wn = wn;
+  g_gtune[stage].ns = ns;
+  g_gtune[stage].ksplit = ksplit;
   return ok();
 }
 

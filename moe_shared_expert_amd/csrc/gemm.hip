@@ -1,0 +1,393 @@
+// LDS-tiled bf16 MFMA GEMM for the gate_up and down stages at larger token counts.
+//
+// C[M, N] = A[M, K] . B[N, K]^T with both operands K-contiguous (A = x or h, B = the
+// weight rows).  A workgroup computes a BM x BN tile of C over a K slice; WM x WN waves
+// each own a (BM/WM) x (BN/WN) sub-tile built from 32x32x16 bf16 MFMAs with fp32
+// accumulation.
+//
+// Operands reach LDS by direct buffer-to-LDS loads: one 16-byte load instruction of a
+// wave fills a 1 KB block of LDS with 8 tile rows x 128 bytes (one 64-element K step),
+// lane p writing slot p.  Lanes pick their global chunk so that slot s of row r holds
+// K chunk (s % 8) ^ ((r / 2) % 8); a wave's 8 lanes of a row still cover that row's
+// whole 128-byte line, and the sixteen rows read by a quarter-wave for one MFMA
+// fragment fall in distinct LDS banks.  No staging registers are needed, so a wave can
+// hold a 128 x 128 accumulator tile.  LDS is a ring of NS stages: the loads for step
+// k+NS-1 are issued right after the barrier that opens step k, so NS-1 steps of loads
+// are in flight while step k is multiplied.
+// Rows past M or N and K past the slice use out-of-range buffer offsets, which load
+// zeros and move no bytes.
+//
+// gate_up: the B rows of each wave hold a block of gate rows followed by the matching
+// up rows, so a feature's gate and up sums land in the same lane and element of two
+// MFMA tiles and SiLU-and-mul is a register operation.  down: A is h as one bf16 plane,
+// or as two planes hi + lo (two MFMAs per fragment).  With a K split over workgroups
+// the raw fp32 sums go to a partial buffer and a finalize kernel applies the epilogue.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2; the
+// tile order gives each XCD a contiguous run of tiles, walked in groups of GROUP_M
+// token tiles, so the workgroups resident on one XCD share A and B tiles in its L2.
+#include "device_common.h"
+#include "internal.h"
+#include "smlp.h"
+
+namespace smlp {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte buffer load of each lane straight into LDS: lane p writes bytes
+// [16p, 16p + 16) of the 1 KB block at `dst` (the same block for the whole wave).
+__device__ __forceinline__ void buf_ld_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 0);
+}
+
+enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2 };
+
+struct GArgs {
+  const uint16_t* a;      // [M, K] bf16 (down, two planes: hi)
+  const uint16_t* a_lo;   // down, two planes: lo plane
+  const uint16_t* b;      // [rows, K] bf16
+  int M, K;
+  int N;                  // output features: h columns (gate_up) or H (down)
+  int up_off;             // gate_up: first up row (= I)
+  int b_rows;             // rows of b
+  int tiles_m, tiles_n;
+  int kslice;             // K elements per workgroup slice (gridDim.y slices)
+  void* out;              // gate_up: h plane(s); down: out [M, N] bf16 or fp32
+  float* part;            // gridDim.y > 1: fp32 partial sums [slices][M][P*N]
+  int out_f32;
+  int h_planes;           // gate_up: planes of h to store (1 or 2)
+};
+
+constexpr int BK = 64;      // K elements per step (128 bytes of a row)
+constexpr int GROUP_M = 8;  // token tiles per group in the tile order
+constexpr int XCDS = 8;
+
+__device__ __forceinline__ void put_h(void* base, int M, int N, int m, int n, float h, int planes) {
+  const uint32_t hi = f2bf(h);
+  uint16_t* p = reinterpret_cast<uint16_t*>(base);
+  p[(size_t)m * N + n] = (uint16_t)hi;
+  if (planes == 2) p[(size_t)M * N + (size_t)m * N + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
+}
+
+// Swizzle of the 16-byte chunks within tile row r.
+__device__ __forceinline__ int chunk_swz(int r) { return (r >> 1) & 7; }
+
+// Workgroup index -> (tile_m, tile_n): XCD-contiguous runs of the tile order, which
+// walks GROUP_M token tiles down each column of weight tiles before moving right.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int tiles = tiles_m * tiles_n;
+  const int per = tiles / XCDS, rem = tiles % XCDS;
+  const int xcd = bid % XCDS, idx = bid / XCDS;
+  // XCD x owns the run starting at x*per + min(x, rem), of length per + (x < rem).
+  const int t = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int group = GROUP_M * tiles_n;
+  const int gi = t / group;
+  const int first = gi * GROUP_M;
+  const int gsize = min(tiles_m - first, GROUP_M);
+  const int in = t - gi * group;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), whose release
+// semantics would wait for every load in flight, the later steps' LDS loads included.
+// The LDS reads of a step are all consumed by its MFMAs (so complete) before the
+// barrier; the empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most `later` steps of LPS loads each are still in flight.
+template <int LPS, int MAXL>
+__device__ __forceinline__ void wait_steps(int later) {
+  if constexpr (MAXL == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXL) wait_vmcnt<MAXL * LPS>();
+    else wait_steps<LPS, MAXL - 1>(later);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int MODE>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
+  constexpr bool GU = MODE == GM_GATE_UP;
+  constexpr int NA = MODE == GM_DOWN_HILO ? 2 : 1;
+  constexpr int W = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
+  constexpr int AL = BM / 8 / W, BL = BN / 8 / W;      // 1 KB block loads per wave per step
+  static_assert(AL * W * 8 == BM && BL * W * 8 == BN, "tile / wave mismatch");
+  static_assert(!GU || TN % 2 == 0, "gate_up pairs gate and up MFMA tiles");
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  constexpr int STAGE = NA * A_BYTES + B_BYTES;
+  constexpr int LPS = NA * AL + BL;  // load instructions per wave per step
+  static_assert(NS >= 2 && LPS * (NS - 2) < 64, "stage count");
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+  int tile_m, tile_n;
+  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tile_m, tile_n);
+  const int K = g.K;
+  const int kbeg = blockIdx.y * g.kslice;
+  const int kend = min(K, kbeg + g.kslice);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  const uint32_t abytes = (uint32_t)g.M * (uint32_t)K * 2u;
+  const uint32_t bbytes = (uint32_t)g.b_rows * (uint32_t)K * 2u;
+  const __amdgpu_buffer_rsrc_t arsc[2] = {make_rsrc(g.a, abytes), make_rsrc(NA == 2 ? g.a_lo : g.a, abytes)};
+  const __amdgpu_buffer_rsrc_t brsc = make_rsrc(g.b, bbytes);
+
+  // This lane's slot in each 1 KB block: row p/8, holding global chunk (p%8) ^ swizzle.
+  // Block i of this wave covers tile rows (i*W + wave)*8 .. +7.
+  const int prow = lane >> 3;
+  uint32_t aoff[AL], boff[BL];
+  int achk[AL], bchk[BL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int r = (i * W + wave) * 8 + prow;
+    achk[i] = (lane & 7) ^ chunk_swz(r);
+    const int m = tile_m * BM + r;
+    aoff[i] = m < g.M ? (uint32_t)m * (uint32_t)K * 2u + achk[i] * 16 : abytes;
+  }
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    const int r = (i * W + wave) * 8 + prow;
+    bchk[i] = (lane & 7) ^ chunk_swz(r);
+    int row;
+    bool ok;
+    if (GU) {
+      // Each wave column's 32*TN rows: 16*TN gate rows, then the matching up rows.
+      const int wc = r / (32 * TN), rr = r % (32 * TN);
+      const int f = tile_n * (BN / 2) + wc * 16 * TN + rr % (16 * TN);
+      ok = f < g.N;
+      row = rr < 16 * TN ? f : g.up_off + f;
+    } else {
+      row = tile_n * BN + r;
+      ok = row < g.N;
+    }
+    boff[i] = ok ? (uint32_t)row * (uint32_t)K * 2u + bchk[i] * 16 : bbytes;
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Issue one step's loads into stage `buf` (K elements k0 .. k0+63 of the slice).
+  auto issue = [&](int buf, int k0) {
+    char* st = lds + buf * STAGE;
+    const uint32_t kb = (uint32_t)k0 * 2u;
+#pragma unroll
+    for (int q = 0; q < NA; ++q)
+#pragma unroll
+      for (int i = 0; i < AL; ++i) {
+        const bool ok = aoff[i] != abytes && k0 + achk[i] * 8 < kend;
+        buf_ld_lds(arsc[q], st + q * A_BYTES + (i * W + wave) * 1024, ok ? aoff[i] + kb : abytes);
+      }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const bool ok = boff[i] != bbytes && k0 + bchk[i] * 8 < kend;
+      buf_ld_lds(brsc, st + NA * A_BYTES + (i * W + wave) * 1024, ok ? boff[i] + kb : bbytes);
+    }
+  };
+
+  // 32x32x16 fragments: lane l reads tile row (base + l%32), K chunk 2*ks + l/32.  The
+  // fragments of sub-step ks+1 are read while the MFMAs of sub-step ks run.
+  const int fr = lane & 31, fh = lane >> 5;
+  const int fsw = chunk_swz(fr);  // row bases are multiples of 32
+  constexpr int NFRAG = NA * TM + TN;
+  auto compute = [&](int buf) {
+    const char* st = lds + buf * STAGE;
+    u32x4 fa[2][NA][TM], fb[2][TN];
+    auto read_frags = [&](int slot, int ks) {
+      const int coff = ((2 * ks + fh) ^ fsw) * 16;
+#pragma unroll
+      for (int q = 0; q < NA; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          fa[slot][q][i] = *reinterpret_cast<const u32x4*>(st + q * A_BYTES + ((wm * TM + i) * 32 + fr) * 128 + coff);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[slot][j] = *reinterpret_cast<const u32x4*>(st + NA * A_BYTES + ((wn * TN + j) * 32 + fr) * 128 + coff);
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cur = ks & 1;
+      if (ks < 3) read_frags(cur ^ 1, ks + 1);
+#pragma unroll
+      for (int q = 0; q < NA; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[cur][q][i], fb[cur][j], acc[i][j]);
+      if (ks < 3) {
+        // Interleave: one fragment read, then a share of the MFMAs.
+#pragma unroll
+        for (int t = 0; t < NFRAG; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, NA * TM * TN / NFRAG, 0);  // MFMA
+        }
+      }
+    }
+  };
+
+  // NS-stage ring: step kt lives in stage kt % NS; loads run NS-1 steps ahead.
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, kbeg + st * BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Step kt's loads have landed (this wave: vmcnt, allowing the later steps' loads
+    // to stay in flight; all waves: the barrier), and no wave still reads the stage
+    // that the next loads overwrite (it held step kt-1).
+    wait_steps<LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
+    block_barrier();
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
+    compute(kt % NS);
+  }
+
+  // Epilogue.  32x32 output: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
+  // gate_up: MFMA tile j holds gate features and tile j + TN/2 the matching up rows.
+  const bool split = gridDim.y > 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      // One output row at a time keeps the accumulators from all moving to VGPRs at once.
+      __builtin_amdgcn_sched_barrier(0);
+      const int m = tile_m * BM + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+      if (m >= g.M) continue;
+      if (GU) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int f = tile_n * (BN / 2) + wn * 16 * TN + j * 32 + fr;
+          if (f >= g.N) continue;
+          const float gate = acc[i][j][e], up = acc[i][j + TN / 2][e];
+          if (split) {
+            float* row = g.part + ((size_t)blockIdx.y * g.M + m) * (size_t)(2 * g.N);
+            row[f] = gate;
+            row[g.N + f] = up;
+          } else {
+            put_h(g.out, g.M, g.N, m, f, silu_mul(gate, up), g.h_planes);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = tile_n * BN + (wn * TN + j) * 32 + fr;
+          if (n >= g.N) continue;
+          const float v = acc[i][j][e];
+          if (split)
+            g.part[((size_t)blockIdx.y * g.M + m) * (size_t)g.N + n] = v;
+          else if (g.out_f32)
+            reinterpret_cast<float*>(g.out)[(size_t)m * g.N + n] = v;
+          else
+            reinterpret_cast<uint16_t*>(g.out)[(size_t)m * g.N + n] = (uint16_t)f2bf(v);
+        }
+      }
+    }
+}
+
+// Tile configurations (BM, BN, WM, WN, stages).  LDS holds stages x (BM + BN) x 128
+// bytes (the two-plane down mode: stages x (2 BM + BN) x 128) of the 160 KB per
+// workgroup.
+#define SMLP_GEMM_CONFIGS(X)                                                                    \
+  X(256, 256, 2, 4, 2) X(128, 256, 2, 4, 3) X(128, 256, 2, 2, 3) X(128, 128, 2, 2, 2)           \
+  X(128, 128, 2, 2, 4) X(128, 128, 4, 2, 4) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4) X(128, 64, 4, 1, 6)
+#define SMLP_GEMM_HILO_CONFIGS(X) X(128, 128, 2, 2, 3) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4)
+
+template <int MODE>
+int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
+  const dim3 grid(gp.tiles, gp.ksplit);
+#define SMLP_G(BM_, BN_, WM_, WN_, NS_)                                                          \
+  if (gp.bm == BM_ && gp.bn == BN_ && gp.wm == WM_ && gp.wn == WN_ && gp.ns == NS_) {              \
+    hipLaunchKernelGGL((gemm_kernel<BM_, BN_, WM_, WN_, NS_, MODE>), grid, dim3(WM_ * WN_ * 64), 0, s, a); \
+    return (int)hipGetLastError();                                                               \
+  }
+  if constexpr (MODE == GM_DOWN_HILO) {
+    SMLP_GEMM_HILO_CONFIGS(SMLP_G)
+  } else {
+    SMLP_GEMM_CONFIGS(SMLP_G)
+  }
+#undef SMLP_G
+  return (int)hipErrorInvalidConfiguration;
+}
+
+}  // namespace
+
+bool gemm_instantiated(bool hilo, int bm, int bn, int wm, int wn, int ns) {
+#define SMLP_GM(BM_, BN_, WM_, WN_, NS_) \
+  if (bm == BM_ && bn == BN_ && wm == WM_ && wn == WN_ && ns == NS_) return true;
+  if (hilo) {
+    SMLP_GEMM_HILO_CONFIGS(SMLP_GM)
+  } else {
+    SMLP_GEMM_CONFIGS(SMLP_GM)
+  }
+#undef SMLP_GM
+  return false;
+}
+
+int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s) {
+  GArgs a{};
+  a.a = reinterpret_cast<const uint16_t*>(x);
+  a.a_lo = nullptr;
+  a.b = reinterpret_cast<const uint16_t*>(w_gate_up);
+  a.M = (int)p.M;
+  a.K = (int)p.H;
+  a.N = (int)p.I;
+  a.up_off = (int)p.I;
+  a.b_rows = (int)(2 * p.I);
+  a.tiles_m = p.ggu.tiles_m;
+  a.tiles_n = p.ggu.tiles / p.ggu.tiles_m;
+  a.kslice = p.ggu.kslice;
+  a.out = static_cast<char*>(ws) + p.h_offset;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
+  a.out_f32 = 0;
+  a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
+  int rc = launch_mode<GM_GATE_UP>(p.ggu, a, s);
+  if (rc || p.ggu.ksplit == 1) return rc;
+  return launch_finalize(true, a.part, p.ggu.ksplit, a.M, a.N, a.out, 0, a.h_planes, s);
+}
+
+int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
+  GArgs a{};
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.h_offset);
+  a.a = h;
+  a.a_lo = h + (size_t)p.M * p.I;
+  a.b = reinterpret_cast<const uint16_t*>(w_down);
+  a.M = (int)p.M;
+  a.K = (int)p.I;
+  a.N = (int)p.H;
+  a.up_off = 0;
+  a.b_rows = (int)p.H;
+  a.tiles_m = p.gdn.tiles_m;
+  a.tiles_n = p.gdn.tiles / p.gdn.tiles_m;
+  a.kslice = p.gdn.kslice;
+  a.out = out;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
+  a.out_f32 = p.partial_fp32 ? 1 : 0;
+  a.h_planes = 1;
+  int rc = p.h_dtype == SMLP_BF16_HILO ? launch_mode<GM_DOWN_HILO>(p.gdn, a, s)
+                                      : launch_mode<GM_DOWN_BF16>(p.gdn, a, s);
+  if (rc || p.gdn.ksplit == 1) return rc;
+  return launch_finalize(false, a.part, p.gdn.ksplit, a.M, a.N, out, a.out_f32, 1, s);
+}
+
+}  // namespace smlp

@@ -23,10 +23,15 @@ struct SkinnyPlan {
 
 enum { SKINNY_LDS16 = 1, SKINNY_DIRECT16 = 2 };
 
-// One stage of the LDS-tiled MFMA path.
-struct TiledPlan {
-  int bm, bn;    // output tile (rows of x / h, output features)
-  int blocks;
+// One stage of the LDS-tiled GEMM path (gemm.hip).
+struct GemmPlan {
+  int bm, bn;    // tile: tokens x weight rows (gate_up: bn/2 features)
+  int wm, wn;    // wave grid
+  int ns;        // LDS stages
+  int tiles_m;   // tiles along M (tiles = tiles_m * tiles along N)
+  int tiles;
+  int ksplit;    // workgroups along K
+  int kslice;    // K elements per slice (multiple of 64)
 };
 
 struct Plan {
@@ -34,12 +39,12 @@ struct Plan {
   int64_t M, H, I;
   int dtype;
   int partial_fp32;
-  int h_dtype;              // SMLP_FP32 or SMLP_BF16
+  int h_dtype;              // SMLP_FP32, SMLP_BF16 or SMLP_BF16_HILO
   size_t h_offset, h_bytes;
   size_t part_offset, part_bytes;   // split-K partial sums
   size_t workspace_bytes;
   SkinnyPlan gu, dn;
-  TiledPlan tgu, tdn;
+  GemmPlan ggu, gdn;
   int kernels;
 };
 
@@ -49,10 +54,15 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
                           hipStream_t s);
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
 
-// LDS-tiled MFMA stages (tiled.hip).
-int launch_tiled_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
-                         hipStream_t s);
-int launch_tiled_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
+// Sum K-split partials [ksplit][M][P*N] in slice order and apply the stage epilogue
+// (gate_up: SiLU-and-mul into h with `h_planes` bf16 planes; down: bf16 or fp32 out).
+int launch_finalize(bool gate_up, const float* part, int ksplit, int M, int N, void* out,
+                    int out_f32, int h_planes, hipStream_t s);
+
+// LDS-tiled GEMM stages (gemm.hip).
+bool gemm_instantiated(bool hilo, int bm, int bn, int wm, int wn, int ns);
+int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s);
+int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
 
 // fp32 stages and helpers (aux.hip).
 int launch_fp32_gate_up(const Plan& p, const float* x, const float* w_gate_up, void* ws,

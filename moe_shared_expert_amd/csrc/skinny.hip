@@ -546,7 +546,7 @@ static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
   return (int)hipErrorInvalidConfiguration;
 }
 
-static int finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int out_f32,
+int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int out_f32,
                     int h_planes, hipStream_t s) {
   const size_t total = (size_t)M * N;
   int blocks = (int)((total + 255) / 256);
@@ -579,7 +579,7 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.w_rows = (int)(2 * p.I);
   int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
   if (rc || p.gu.ksplit == 1) return rc;
-  return finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, 0, a.h_planes, s);
+  return launch_finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, 0, a.h_planes, s);
 }
 
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
@@ -601,7 +601,7 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.w_rows = (int)p.H;
   int rc = launch_stage<MODE_DOWN_HILO>(p.dn, a, s);
   if (rc || p.dn.ksplit == 1) return rc;
-  return finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.out_f32, 1, s);
+  return launch_finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.out_f32, 1, s);
 }
 
 }  // namespace smlp

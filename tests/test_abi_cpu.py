@@ -45,6 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_tuning_hook(L):
+    prev = binding.shared_mlp_set_large_m_threshold(129)   # M <= 128 on the streaming path
     try:
         binding.shared_mlp_tune_skinny(0, kind=1, nb=2, waves=8, u=1, ksplit=3)
         p = binding.shared_mlp_plan(16, H, I)
@@ -66,6 +67,32 @@ def test_tuning_hook(L):
             binding.shared_mlp_tune_skinny(2)
     finally:
         binding.shared_mlp_tune_skinny(0)
+        binding.shared_mlp_set_large_m_threshold(prev)
+
+
+def test_default_threshold_and_gemm_tuning(L):
+    # default dispatch: 32 tokens stream the weights, 33 take the tiled path
+    assert binding.shared_mlp_plan(32, H, I)["path_name"] == "small_m"
+    assert binding.shared_mlp_plan(33, H, I)["path_name"] == "large_m"
+    # prefill: 256 x 256 tiles, one per workgroup, no K split
+    p = binding.shared_mlp_plan(8192, H, I)
+    assert p["gate_up_blocks"] == (8192 // 256) * (2 * I // 256) and p["gate_up_ksplit"] == 1
+    assert p["down_blocks"] == (8192 // 256) * (H // 256) and p["down_ksplit"] == 1
+    try:
+        binding.shared_mlp_tune_gemm(0, bm=128, bn=128, wm=2, wn=2, ns=4, ksplit=2)
+        p = binding.shared_mlp_plan(512, H, I)
+        assert p["gate_up_ksplit"] == 2 and p["gate_up_blocks"] == 2 * (512 // 128) * (2 * I // 128)
+        binding.shared_mlp_tune_gemm(0, bm=128, bn=128, wm=2, wn=2, ns=5)   # not compiled
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_plan(512, H, I)
+        for bad in (dict(bm=96, bn=128), dict(bm=128, bn=0), dict(bm=128, bn=128, wm=3, wn=1),
+                    dict(ns=9), dict(ksplit=-1)):
+            with pytest.raises(binding.SmlpError):
+                binding.shared_mlp_tune_gemm(0, **bad)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_gemm(2)
+    finally:
+        binding.shared_mlp_tune_gemm(0)
 
 
 def test_status_strings(L):
