@@ -2,12 +2,13 @@
  * smlp_tuning.h -- tuning hook of libsmlp's M-dispatch planner (not needed for use).
  *
  * The weight-streaming (small-M) stages are parameterised by the kernel kind (kind:
- * 1 = operands staged through LDS, M <= 32 only; 2 = operands loaded directly in the
- * MFMA layout), the number of 16-feature blocks per workgroup (nb), waves per
- * workgroup (waves), 64-element K steps per wave per pipeline stage (u) and the K
- * split over workgroups (ksplit).  By default the planner picks them from M, N and K.  This hook pins any of them (0 = automatic) for
- * subsequent plans, process-wide, so a benchmark can sweep them.  Results are the
- * same up to fp32 summation order.
+ * 2 = operands loaded directly in the MFMA layout; 3 = operands streamed into a
+ * wave-private LDS ring, M <= 32 only), the number of 16-feature blocks per
+ * workgroup (nb), waves per workgroup (waves), u (kind 2: 64-element K steps per wave
+ * per pipeline stage; kind 3: LDS ring stages) and the K split over workgroups
+ * (ksplit).  By default the planner picks them from M, N and K.  This hook pins any
+ * of them (0 = automatic) for subsequent plans, process-wide, so a benchmark can sweep
+ * them.  Results are the same up to fp32 summation order.
  */
 #ifndef SMLP_TUNING_H
 #define SMLP_TUNING_H
@@ -15,8 +16,8 @@
 extern "C" {
 #endif
 
-/* stage: 0 = gate_up, 1 = down.  kind in {0,1,2}; nb in {0,1,2,4}; waves in {0,4,8};
- * u in {0,1,2}; 0 <= ksplit <= 1024.  Returns SMLP_OK or SMLP_ERR_ARG.  A pinned
+/* stage: 0 = gate_up, 1 = down.  kind in {0,2,3}; nb in {0,1,2,4}; waves in {0,4,8};
+ * u in {0,...,5}; 0 <= ksplit <= 1024.  Returns SMLP_OK or SMLP_ERR_ARG.  A pinned
  * combination that is not a compiled kernel makes later plans fail with SMLP_ERR_ARG. */
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit);
 

@@ -73,7 +73,7 @@ struct GemmOverride {
 };
 GemmOverride g_gtune[2];
 
-// Small-M stage plan.  M <= 32: the LDS-staged kernel, one workgroup per compute unit
+// Small-M stage plan.  M <= 32: the streaming kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
 // range, waves interleaved over K.  M > 32: the direct-load kernel over 16-feature
 // blocks, with a K split over workgroups when the blocks alone cannot keep about
@@ -83,12 +83,14 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
   using namespace smlp;
   const SkinnyOverride& o = g_tune[stage];
   smlp::SkinnyPlan sp{};
-  sp.kind = o.kind.load() ? o.kind.load() : (M <= 32 ? SKINNY_LDS16 : SKINNY_DIRECT16);
-  if (sp.kind == SKINNY_LDS16 && M > 32) return false;
+  sp.kind = o.kind.load() ? o.kind.load() : (M <= 32 ? SKINNY_STREAM16 : SKINNY_DIRECT16);
+  sp.waves = 0;
+  if (sp.kind == SKINNY_STREAM16 && M > 32) return false;
   sp.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  // u: LDS ring stages of the streaming kind, the unroll of the direct kind.
   sp.u = o.u.load() ? o.u.load() : 1;
   const int64_t ksteps = (K + 63) / 64;
-  if (sp.kind == SKINNY_LDS16) {
+  if (sp.kind == SKINNY_STREAM16) {
     const int64_t tile = stage == 0 ? 8 : 16;  // features per 16-row tile
     int64_t groups = o.nb.load() ? (N + tile * o.nb.load() - 1) / (tile * o.nb.load()) : kCUs;
     if (groups > N) groups = N;
@@ -101,7 +103,26 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     groups = (N + fpw - 1) / fpw;
     sp.nb = (int)nt;
     sp.fpw = (int)fpw;
-    sp.waves = o.waves.load() ? o.waves.load() : (ksteps >= 64 ? 8 : 4);
+    // Measured on MI355X: gate_up is fastest with 4 waves and a 3-stage ring, down
+    // with 8 waves and 2 stages; otherwise the first compiled (waves, stages) pair in
+    // this order.
+    static const int kPrefGU[][2] = {{4, 3}, {4, 4}, {4, 2}, {8, 2}};
+    static const int kPrefDN[][2] = {{8, 2}, {8, 3}, {4, 4}, {4, 3}, {4, 2}};
+    const int (*pref)[2] = stage == 0 ? kPrefGU : kPrefDN;
+    const int npref = stage == 0 ? 4 : 5;
+    if (!o.waves.load() || !o.u.load()) {
+      for (int c = 0; c < npref; ++c) {
+        const int w = o.waves.load() ? o.waves.load() : pref[c][0];
+        const int st = o.u.load() ? o.u.load() : pref[c][1];
+        if (smlp::skinny_instantiated(stage == 0, sp.kind, sp.mt, (int)nt, w, st)) {
+          sp.waves = w;
+          sp.u = st;
+          break;
+        }
+      }
+    }
+    if (o.waves.load()) sp.waves = o.waves.load();
+    if (o.u.load()) sp.u = o.u.load();
     int64_t ks = o.ksplit.load() ? o.ksplit.load() : 1;
     if (ks > ksteps) ks = ksteps;
     const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
@@ -438,8 +459,8 @@ int64_t shared_mlp_set_large_m_threshold(int64_t threshold) {
 }
 
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit) {
-  if (stage < 0 || stage > 1 || kind < 0 || kind > 2 || !(nb == 0 || nb == 1 || nb == 2 || nb == 4) ||
-      !(waves == 0 || waves == 4 || waves == 8) || u < 0 || u > 2 || ksplit < 0 || ksplit > 1024)
+  if (stage < 0 || stage > 1 || kind < 0 || kind == 1 || kind > 3 || !(nb == 0 || nb == 1 || nb == 2 || nb == 4) ||
+      !(waves == 0 || waves == 4 || waves == 8) || u < 0 || u > 5 || ksplit < 0 || ksplit > 1024)
     return fail(SMLP_ERR_ARG, "bad small-M tuning (stage %d kind %d nb %d waves %d u %d ksplit %d)",
                 stage, kind, nb, waves, u, ksplit);
   g_tune[stage].kind = kind;

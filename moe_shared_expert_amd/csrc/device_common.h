@@ -61,6 +61,25 @@ __device__ __forceinline__ u32x4 buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// 16-byte buffer loads of each lane straight into LDS: lane p of the wave writes bytes
+// [16p, 16p + 16) of the 1 KB block at `dst` (one block for the whole wave; the
+// address must be wave-uniform).  Out-of-range offsets write zeros.  Completion is
+// tracked by vmcnt like any vector memory load.  Non-temporal and default policy.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void buf_ld_lds_nt(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 2);
+}
+__device__ __forceinline__ void buf_ld_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
 // 16-byte global loads.  Weights are read exactly once per call, so they are loaded
 // non-temporally; activations are re-read by many workgroups and use normal loads.
 __device__ __forceinline__ u32x4 ld_stream(const void* p) {

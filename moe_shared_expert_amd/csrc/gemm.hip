@@ -34,13 +34,6 @@ namespace smlp {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16-byte buffer load of each lane straight into LDS: lane p writes bytes
-// [16p, 16p + 16) of the 1 KB block at `dst` (the same block for the whole wave).
-__device__ __forceinline__ void buf_ld_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 0);
-}
 
 enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2 };
 
@@ -89,13 +82,6 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   const int in = t - gi * group;
   tm = first + in % gsize;
   tn = in / gsize;
-}
-
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(), whose release

@@ -9,19 +9,20 @@ namespace smlp {
 // One weight-streaming (small-M) stage: out-features in blocks of 16, K split into
 // `ksplit` slices over workgroups and into `waves` slices inside a workgroup.
 struct SkinnyPlan {
-  int kind;      // SKINNY_LDS16 or SKINNY_DIRECT16
+  int kind;      // SKINNY_STREAM16 or SKINNY_DIRECT16
   int mt;        // 16-token tiles (M <= 16 * mt)
-  int nb;        // output tiles per workgroup (SKINNY_LDS16: 16-row MFMA tiles holding
+  int nb;        // output tiles per workgroup (SKINNY_STREAM16: 16-row MFMA tiles holding
                  // 8 gate_up features or 16 down rows; SKINNY_DIRECT16: 16-feature blocks)
   int waves;     // waves per workgroup (they split K)
-  int u;         // 64-element K steps per wave per pipeline stage
+  int u;         // SKINNY_STREAM16: LDS ring stages; SKINNY_DIRECT16: 64-element K steps
+                 // per wave per pipeline stage
   int ksplit;    // workgroups along K (1 = no cross-workgroup reduction)
   int kslice;    // K elements per workgroup slice (multiple of 64)
   int blocks;    // total workgroups
-  int fpw;       // SKINNY_LDS16: features (gate_up) or rows (down) per workgroup
+  int fpw;       // SKINNY_STREAM16: features (gate_up) or rows (down) per workgroup
 };
 
-enum { SKINNY_LDS16 = 1, SKINNY_DIRECT16 = 2 };
+enum { SKINNY_DIRECT16 = 2, SKINNY_STREAM16 = 3 };
 
 // One stage of the LDS-tiled GEMM path (gemm.hip).
 struct GemmPlan {

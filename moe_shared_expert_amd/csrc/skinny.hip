@@ -9,19 +9,18 @@
 //
 // Memory access: the MFMA operand layout puts 16 different rows in the 16 lanes of
 // each lane group, so loading operands directly in that layout makes every load
-// instruction touch 16 cache lines (64 bytes of each).  Measured on MI355X that
-// caps streaming at ~4-5 TB/s; loading 8 rows x 128 contiguous bytes per instruction
-// (8 full lines) reaches ~6.5 TB/s.  Each wave therefore loads 64-element K steps of
-// its weight rows and activation rows in the 8-row layout, writes them to a
-// wave-private LDS tile (rows padded to 144 bytes, so both the writes and the
-// fragment reads are bank-conflict-light) and reads the MFMA fragments back.  No
-// other wave touches the tile, so no barrier is needed.
-//
-// Loads are software pipelined two stages deep (the next stage's loads are issued
-// before the current stage is written to LDS and multiplied).  The K range of a
-// workgroup is interleaved over its waves in 64-element steps and reduced through
-// LDS in a fixed tree order; a K split over workgroups (for shapes with few feature
-// blocks) is reduced by a second, elementwise kernel that also applies the epilogue.
+// instruction touch 16 cache lines (64 bytes of each).  Measured on MI355X that caps
+// streaming at ~4-5 TB/s; loading 8 rows x 128 contiguous bytes per instruction (8
+// full lines) streams at the rate of a plain linear read.  For M <= 32 the streaming
+// kernel therefore moves each 64-element K step of a wave's weight and activation
+// rows in that 8-row layout straight into a wave-private LDS ring (direct
+// buffer-to-LDS loads, chunks XOR-swizzled so the MFMA fragment reads are free of
+// bank conflicts) and keeps several K steps in flight with explicit vmcnt waits.  For
+// larger M the direct kernel loads MFMA operands straight into registers.  The K
+// range of a workgroup is interleaved over its waves in 64-element steps and reduced
+// through LDS in a fixed tree order; a K split over workgroups (for shapes with few
+// feature blocks) is reduced by a second, elementwise kernel that also applies the
+// epilogue.
 //
 // The intermediate h is handed from gate_up to down as two bf16 planes, hi = rne(h)
 // and lo = rne(h - hi), which together carry ~16 significant bits; the down kernel
@@ -132,31 +131,36 @@ __device__ __forceinline__ void finish_workgroup(const SkArgs& a,
     }
 }
 
-// LDS-staged kernel (M <= 32).  A workgroup owns the contiguous feature range
-// [blockIdx.x * fpw, +fpw) and a K slice; the range is cut into NT 16-row MFMA tiles.
-// gate_up tiles pack 8 features: rows 0-7 are their gate rows and rows 8-15 their up
-// rows, so each tile is exactly two 8-row x 128-byte loads; down tiles are 16
-// consecutive rows.  All loads are raw buffer loads: rows past the range, tokens past
-// M and K past the slice get an out-of-range offset, which yields zeros and moves no
-// bytes, so the loop has no branches and no separate tail.
-template <int MT, int NT, int WAVES, int MODE>
-__global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
+// Streaming kernel (M <= 32).  Same work split as the LDS-staged kernel, but each
+// operand block reaches a wave-private LDS ring by direct buffer-to-LDS loads: a
+// 16-byte load per lane fills 1 KB with 8 rows x 128 bytes (one 64-element K step),
+// lane p writing slot p, the lane choosing its global chunk so that slot s of row r
+// holds chunk (s % 8) ^ ((r / 2) % 8) and the 16-row fragment reads are free of bank
+// conflicts.  No registers hold loads in flight, so the ring can keep STAGES - 1 K
+// steps of loads in flight per wave, with explicit vmcnt waits; the ring is private
+// to the wave, so the loop needs no barrier.  Steps past the slice load zeros (no
+// memory traffic), so the loop issues ahead without branches.
+template <int MT, int NT, int WAVES, int STAGES, int MODE>
+__global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   constexpr bool GU = MODE == MODE_GATE_UP;
-  constexpr int NA = GU ? 1 : 2;                      // activation planes: x, or h hi + lo
-  constexpr int TA = NA * MT;                         // activation tiles per K step
-  constexpr int TT = NT + TA;
-  constexpr int ROWB = 144;                           // padded LDS row: 128 data bytes + 16
-  constexpr int TILEB = 16 * ROWB;
-  constexpr int STAGE_LDS = WAVES * TT * TILEB;
+  constexpr int NA = GU ? 1 : 2;        // activation planes: x, or h hi + lo
+  constexpr int TA = NA * MT;           // activation tiles per K step
+  constexpr int TT = NT + TA;           // 2 KB tiles per K step
+  constexpr int SLOT = TT * 2048;       // one ring slot: one K step of this wave
+  constexpr int WAVE_LDS = STAGES * SLOT;
+  constexpr int LPS = 2 * TT;           // 1 KB loads per K step
   constexpr int RED_LDS = lds_red_bytes<MT, NT, WAVES, false>();
-  __shared__ __attribute__((aligned(16))) char lds[STAGE_LDS > RED_LDS ? STAGE_LDS : RED_LDS];
+  constexpr int LDS_BYTES = WAVES * WAVE_LDS > RED_LDS ? WAVES * WAVE_LDS : RED_LDS;
+  static_assert(STAGES >= 2 && LPS * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;
-  const int lr = lane >> 3, lc = lane & 7;  // 8-row load layout: row, 16-byte chunk
+  const int lr = lane >> 3;  // row within a 1 KB block
   const int K = a.K;
-  char* my = lds + wave * (TT * TILEB);
+  char* my = lds + wave * WAVE_LDS;
 
   const int f0 = blockIdx.x * a.fpw;
   const int fend = min(a.N, f0 + a.fpw);
@@ -165,7 +169,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, wbytes);
   const __amdgpu_buffer_rsrc_t ar[2] = {make_rsrc(a.a_hi, abytes), make_rsrc(NA == 2 ? a.a_lo : a.a_hi, abytes)};
 
-  // Per-lane row byte offsets (chunk included) or the out-of-range marker.
+  // Block h of a tile holds tile rows 8h .. 8h+7; this lane loads row 8h + lr, chunk
+  // ch[h].  Per-lane row byte offsets (chunk included) or the out-of-range marker.
+  int ch[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) ch[h] = (lane & 7) ^ (((8 * h + lr) >> 1) & 7);
   uint32_t wo[NT][2], ao[TA][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -174,14 +182,14 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
       int row;
       bool ok;
       if (GU) {
-        const int f = f0 + 8 * t + lr;
+        const int f = f0 + 8 * t + lr;  // rows 0-7: gate rows, rows 8-15: the matching up rows
         ok = f < fend;
         row = h ? a.up_off + f : f;
       } else {
         row = f0 + 16 * t + 8 * h + lr;
         ok = row < fend;
       }
-      wo[t][h] = ok ? (uint32_t)row * (uint32_t)K * 2u + lc * 16 : wbytes;
+      wo[t][h] = ok ? (uint32_t)row * (uint32_t)K * 2u + ch[h] * 16 : wbytes;
     }
 #pragma unroll
   for (int q = 0; q < NA; ++q)
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int m = mt * 16 + 8 * h + lr;
-        ao[q * MT + mt][h] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + lc * 16 : abytes;
+        ao[q * MT + mt][h] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + ch[h] * 16 : abytes;
       }
 
   f32x4 acc[NT][MT];
@@ -204,44 +212,39 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
   constexpr int STEP = 64 * WAVES;
   const int nst = (kend - kbeg + STEP - 1) / STEP;
 
-  struct Stage {
-    u32x4 w[NT][2];
-    u32x4 x[TA][2];
-  };
-  auto load = [&](Stage& s, int i) {
+  // Issue K step i of this wave into ring slot `slot`.
+  auto issue = [&](int slot, int i) {
     const int k = kbeg + (i * WAVES + wave) * 64;
-    const bool kok = k + lc * 8 < kend;
     const uint32_t kb = (uint32_t)k * 2u;
+    char* sl = my + slot * SLOT;
+    bool kok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kok[h] = k + ch[h] * 8 < kend;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        s.w[t][h] = buf_ld_nt(wr, (kok && wo[t][h] != wbytes) ? wo[t][h] + kb : wbytes);
+        buf_ld_lds_nt(wr, sl + t * 2048 + h * 1024, (kok[h] && wo[t][h] != wbytes) ? wo[t][h] + kb : wbytes);
 #pragma unroll
     for (int t = 0; t < TA; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        s.x[t][h] = buf_ld(ar[t / MT], (kok && ao[t][h] != abytes) ? ao[t][h] + kb : abytes);
+        buf_ld_lds(ar[t / MT], sl + (NT + t) * 2048 + h * 1024,
+                   (kok[h] && ao[t][h] != abytes) ? ao[t][h] + kb : abytes);
   };
-  auto compute = [&](const Stage& s) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(my + t * TILEB + (8 * h + lr) * ROWB + lc * 16) = s.w[t][h];
-#pragma unroll
-    for (int t = 0; t < TA; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(my + (NT + t) * TILEB + (8 * h + lr) * ROWB + lc * 16) = s.x[t][h];
+  // Multiply the K step in ring slot `slot`: 16x16x32 fragments, lane (ln, lg) reads
+  // tile row ln, chunk 4j + lg.
+  const int fsw = (ln >> 1) & 7;
+  auto compute = [&](int slot) {
+    const char* sl = my + slot * SLOT;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int foff = ln * ROWB + (4 * j + lg) * 16;
+      const int off = ln * 128 + (((4 * j + lg) ^ fsw) * 16);
       u32x4 fb[NT], fa[TA];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) fb[t] = *reinterpret_cast<const u32x4*>(my + t * TILEB + foff);
+      for (int t = 0; t < NT; ++t) fb[t] = *reinterpret_cast<const u32x4*>(sl + t * 2048 + off);
 #pragma unroll
-      for (int t = 0; t < TA; ++t) fa[t] = *reinterpret_cast<const u32x4*>(my + (NT + t) * TILEB + foff);
+      for (int t = 0; t < TA; ++t) fa[t] = *reinterpret_cast<const u32x4*>(sl + (NT + t) * 2048 + off);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -251,25 +254,22 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_lds_kernel(SkArgs a) {
     }
   };
 
-  // Two-stage software pipeline, unrolled by two so that the stage buffers alternate
-  // without register copies.  Stages past the slice load zeros (no memory traffic),
-  // so the trip count is rounded up to even without a branch.  sched_barrier keeps
-  // every load of the next stage issued before the current stage is consumed.
-  Stage s0, s1;
-  load(s0, 0);
-  for (int i = 0; i < nst; i += 2) {
-    load(s1, i + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(s0, i + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p) issue(p, p);
+  int slot = 0;  // ring slot of step i
+  for (int i = 0; i < nst; ++i) {
+    // The slot of step i - 1 (multiplied in the previous iteration) takes step
+    // i + STAGES - 1; then wait until step i has landed, STAGES - 1 later steps may
+    // stay in flight.
+    issue(slot == 0 ? STAGES - 1 : slot - 1, i + STAGES - 1);
+    wait_vmcnt<LPS * (STAGES - 1)>();
+    compute(slot);
+    slot = slot == STAGES - 1 ? 0 : slot + 1;
   }
+  wait_vmcnt<0>();  // the loads issued past the end write zeros into the ring
 
-  // Reduce the WAVES K-shares of the workgroup through LDS (reusing the staging
-  // tiles), as a fixed binary tree.
+  // Reduce the WAVES K-shares of the workgroup through LDS (reusing the ring), as a
+  // fixed binary tree.
   if constexpr (WAVES > 1) {
     f32x4* red = reinterpret_cast<f32x4*>(lds);
     __syncthreads();
@@ -494,24 +494,28 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
 }
 
 // Instantiated configurations (MT, NB, WAVES, U) per kernel kind (MT = 16-token
-// tiles, NB = 16-feature blocks); none spills registers.
-#define SMLP_SK_LDS16(X)                                                                       \
-  X(1, 1, 4, 1) X(1, 1, 8, 1) X(1, 2, 4, 1) X(1, 2, 8, 1) X(1, 3, 4, 1) X(1, 3, 8, 1)          \
-  X(1, 4, 4, 1) X(1, 4, 8, 1) X(2, 1, 4, 1) X(2, 1, 8, 1) X(2, 2, 4, 1) X(2, 2, 8, 1)          \
-  X(2, 3, 4, 1) X(2, 3, 8, 1) X(2, 4, 4, 1)
-#define SMLP_SK_GU_LDS16(X) SMLP_SK_LDS16(X)
-#define SMLP_SK_DN_LDS16(X) SMLP_SK_LDS16(X)
+// tiles, NB = 16-feature blocks; U = register stages for the LDS-staged kind, the
+// unroll for the direct kind); none spills registers.
+// Streaming kind (MT, NB, WAVES, STAGES): LDS = WAVES x STAGES x (NB + activation
+// tiles) x 2 KB <= 160 KB, activation tiles = MT (gate_up) or 2 MT (down).
+#define SMLP_SK_GU_STREAM16(X)                                                                 \
+  X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 2, 4, 4) X(1, 2, 8, 3) X(1, 3, 4, 3) X(1, 3, 4, 4)          \
+  X(1, 3, 4, 5) X(1, 3, 8, 2) X(1, 4, 4, 4) X(2, 1, 4, 4) X(2, 2, 4, 4) X(2, 3, 4, 3)          \
+  X(2, 3, 4, 4) X(2, 4, 4, 3)
+#define SMLP_SK_DN_STREAM16(X)                                                                 \
+  X(1, 1, 4, 4) X(1, 1, 8, 3) X(1, 2, 4, 3) X(1, 2, 4, 4) X(1, 2, 4, 5) X(1, 2, 8, 2)          \
+  X(1, 3, 4, 4) X(1, 4, 4, 3) X(2, 1, 4, 4) X(2, 2, 4, 3) X(2, 3, 4, 2) X(2, 4, 4, 2)
 #define SMLP_SK_GU_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1) X(8, 1, 8, 1)
 #define SMLP_SK_DN_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1)
 bool skinny_instantiated(bool gu, int kind, int mt, int nb, int waves, int u) {
 #define SMLP_MATCH(MT_, NB_, W_, U_) \
   if (mt == MT_ && nb == NB_ && waves == W_ && u == U_) return true;
   if (gu) {
-    if (kind == SKINNY_LDS16) { SMLP_SK_GU_LDS16(SMLP_MATCH) }
     if (kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_MATCH) }
+    if (kind == SKINNY_STREAM16) { SMLP_SK_GU_STREAM16(SMLP_MATCH) }
   } else {
-    if (kind == SKINNY_LDS16) { SMLP_SK_DN_LDS16(SMLP_MATCH) }
     if (kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_MATCH) }
+    if (kind == SKINNY_STREAM16) { SMLP_SK_DN_STREAM16(SMLP_MATCH) }
   }
 #undef SMLP_MATCH
   return false;
@@ -527,20 +531,20 @@ static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((KERNEL<MT_, NB_, W_, U_, MODE>), grid, block, 0, s, a);          \
     return (int)hipGetLastError();                                                       \
   }
-#define SMLP_SK_L(MT__, NB__, W__, U__)                                                  \
-  if (sp.mt == MT__ && sp.nb == NB__ && sp.waves == W__ && sp.u == U__) {                \
-    hipLaunchKernelGGL((skinny_lds_kernel<MT__, NB__, W__, MODE>), grid, block, 0, s, a); \
-    return (int)hipGetLastError();                                                       \
-  }
 #define SMLP_SK_D(MT__, NB__, W__, U__) { constexpr int MT_ = MT__, NB_ = NB__, W_ = W__, U_ = U__; SMLP_SK(skinny_direct_kernel) }
-  if constexpr (GU) {
-    if (sp.kind == SKINNY_LDS16) { SMLP_SK_GU_LDS16(SMLP_SK_L) }
-    if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_SK_D) }
-  } else {
-    if (sp.kind == SKINNY_LDS16) { SMLP_SK_DN_LDS16(SMLP_SK_L) }
-    if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_SK_D) }
+#define SMLP_SK_S(MT__, NB__, W__, U__)                                                     \
+  if (sp.mt == MT__ && sp.nb == NB__ && sp.waves == W__ && sp.u == U__) {                   \
+    hipLaunchKernelGGL((skinny_stream_kernel<MT__, NB__, W__, U__, MODE>), grid, block, 0, s, a); \
+    return (int)hipGetLastError();                                                          \
   }
-#undef SMLP_SK_L
+  if constexpr (GU) {
+    if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_SK_D) }
+    if (sp.kind == SKINNY_STREAM16) { SMLP_SK_GU_STREAM16(SMLP_SK_S) }
+  } else {
+    if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_SK_D) }
+    if (sp.kind == SKINNY_STREAM16) { SMLP_SK_DN_STREAM16(SMLP_SK_S) }
+  }
+#undef SMLP_SK_S
 #undef SMLP_SK_D
 #undef SMLP_SK
   return (int)hipErrorInvalidConfiguration;

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 def test_tuning_hook(L):
     prev = binding.shared_mlp_set_large_m_threshold(129)   # M <= 128 on the streaming path
     try:
-        binding.shared_mlp_tune_skinny(0, kind=1, nb=2, waves=8, u=1, ksplit=3)
+        binding.shared_mlp_tune_skinny(0, kind=3, nb=2, waves=4, u=4, ksplit=3)
         p = binding.shared_mlp_plan(16, H, I)
         assert p["gate_up_ksplit"] == 3 and p["gate_up_blocks"] == 3 * (I // 16)
         binding.shared_mlp_tune_skinny(0)
@@ -56,13 +56,15 @@ def test_tuning_hook(L):
         binding.shared_mlp_tune_skinny(0, kind=2, nb=1, waves=4, u=1, ksplit=2)
         p = binding.shared_mlp_plan(64, H, I)
         assert p["gate_up_ksplit"] == 2 and p["gate_up_blocks"] == 2 * (I // 16)
-        binding.shared_mlp_tune_skinny(0, kind=1, nb=1, waves=4, u=1, ksplit=1)
+        binding.shared_mlp_tune_skinny(0, kind=3, nb=1, waves=4, u=4, ksplit=1)
         with pytest.raises(binding.SmlpError):
-            binding.shared_mlp_plan(64, H, I)   # the LDS-staged kind serves M <= 32 only
+            binding.shared_mlp_plan(64, H, I)   # the streaming kind serves M <= 32 only
         with pytest.raises(binding.SmlpError):
             binding.shared_mlp_tune_skinny(0, nb=3)
         with pytest.raises(binding.SmlpError):
-            binding.shared_mlp_tune_skinny(0, kind=3)
+            binding.shared_mlp_tune_skinny(0, kind=4)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_skinny(0, kind=1)   # retired kind
         with pytest.raises(binding.SmlpError):
             binding.shared_mlp_tune_skinny(2)
     finally:
