@@ -8,8 +8,9 @@ on inputs already resident in HBM.
 
 Prints one JSON line (rank 0).  ``value`` is the achieved algorithmic HBM bandwidth
 (weights + x + out bytes per layer / time per layer).  ``roofline`` reports the
-dominant kernel (gate_up) timed with HIP events on its stream inside the timed
-region.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+dominant kernel (gate_up + SiLU-and-mul): HIP events on its stream around graph
+replays of back-to-back launches of that stage alone give its average launch
+duration.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
 workload.  ``--sweep`` adds one line per (layout, M) of the M sweep.
 """
 from __future__ import annotations
@@ -64,7 +65,7 @@ def make_inputs(M, I_r, copies, cfg, dev):
 
 def run_workload(name, steps, warmup, dev, launch="graph"):
     """Time `steps` layer forwards (value) and, separately, `steps` launches of the
-    dominant gate_up stage each bracketed by its own event pair (roofline)."""
+    dominant gate_up stage alone, back to back (roofline)."""
     M, I_r, partial, copies, cfg, desc = WORKLOADS[name]
     x, weights = make_inputs(M, I_r, copies, cfg, dev)
     odt = torch.float32 if partial else torch.bfloat16
@@ -77,7 +78,9 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
         g, d = weights[i % copies]
         binding.shared_mlp_forward(x, g, d, out, partial, ws, stream)
 
-    stream = torch.cuda.Stream(dev) if launch == "graph" else torch.cuda.current_stream(dev)
+    # graph capture needs a side stream; eager launches use it too, so that the
+    # dominant-kernel graph below can be captured in both modes
+    stream = torch.cuda.Stream(dev)
     with torch.cuda.stream(stream):
         for i in range(max(warmup, copies)):
             step(i, stream)
@@ -109,16 +112,28 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / n_steps
 
-    # dominant kernel: gate_up + SiLU-and-mul, each launch between its own events
-    kev = [(_ev(), _ev()) for _ in range(steps)]
+    # dominant kernel: gate_up + SiLU-and-mul alone, launched back to back (a graph of one
+    # launch per weight copy, replayed), so the average includes no host or event
+    # overhead -- the figure a kernel trace reports, plus the inter-kernel gap.
+    def gu_only(i, strm):
+        g, _ = weights[i % copies]
+        binding.shared_mlp_gate_up_act(x, g, ws, partial, strm)
+
+    gu_graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
-        for i in range(steps):
-            g, _ = weights[i % copies]
-            kev[i][0].record(stream)
-            binding.shared_mlp_gate_up_act(x, g, ws, partial, stream)
-            kev[i][1].record(stream)
+        with torch.cuda.graph(gu_graph, stream=stream):
+            for i in range(copies):
+                gu_only(i, stream)
     torch.cuda.synchronize()
-    gu_us = 1e3 * sum(a.elapsed_time(b) for a, b in kev) / steps
+    gu_reps = max(1, steps // copies)
+    with torch.cuda.stream(stream):
+        gu_graph.replay()
+        t0.record(stream)
+        for _ in range(gu_reps):
+            gu_graph.replay()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    gu_us = 1e3 * t0.elapsed_time(t1) / (gu_reps * copies)
 
     out_elem = 4 if partial else 2
     alg = roofline.algorithmic_bytes(M, H, I_r, 2, out_elem)

@@ -157,8 +157,8 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
 
 // LDS-tiled GEMM stage plan (measured on MI355X over M = 64 .. 8192, I = 768 and 6144):
 // 256 x 256 tiles (8 waves, 128 x 64 per wave) when they fill the chip at least twice
-// over and K is long; otherwise 128 x 128 tiles (4 waves) for gate_up unless there are
-// very few of them, and for down when they fill the chip twice; else 128 x 64 tiles.
+// over and K is long; otherwise 128 x 128 tiles (4 waves) when they fill the chip
+// (gate_up) or fill it twice (down); else 128 x 64 tiles with a K split.
 // Two LDS stages, so that two workgroups share a compute unit, and a K split over
 // workgroups when the tiles alone leave compute units idle.  N counts gate_up features
 // (two weight rows each) or down rows.  Returns false if a pinned tile is not compiled.
@@ -173,7 +173,7 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!hilo && tiles_for(256, 256) >= 2 * kCUs && K >= 4096) {
     gp.bm = 256;
     gp.bn = 256;
-  } else if (tiles_for(128, 128) >= (stage == 0 ? 64 : 2 * kCUs)) {
+  } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs)) {
     gp.bm = 128;
     gp.bn = 128;
   } else {
@@ -207,7 +207,17 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   const int64_t ksteps = (K + 63) / 64;
   int64_t ks = o.ksplit.load();
   if (!ks) {
-    ks = tiles >= kCUs ? 1 : (kCUs + tiles - 1) / tiles;
+    if (gp.bn == 64 && gp.bm == 128) {
+      // Few weight tiles (medium M): split K until about 3 (gate_up) or 1.75 (down)
+      // workgroups per compute unit stream weights; fp32 partials cost 2 M / K of the
+      // weight traffic per slice, so short K (I of a TP shard) takes at most 3 slices.
+      const int64_t target = stage == 0 ? 3 * kCUs : 7 * kCUs / 4;
+      ks = (target + tiles - 1) / tiles;
+      if (ks > 16) ks = 16;
+      if (K < 2048 && ks > 3) ks = 3;
+    } else {
+      ks = tiles >= kCUs ? 1 : (kCUs + tiles - 1) / tiles;
+    }
     const int64_t max_ks = ksteps / 2;  // at least two 64-element K steps per slice
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;

@@ -24,8 +24,9 @@
 // the raw fp32 sums go to a partial buffer and a finalize kernel applies the epilogue.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2; the
-// tile order gives each XCD a contiguous run of tiles, walked in groups of GROUP_M
-// token tiles, so the workgroups resident on one XCD share A and B tiles in its L2.
+// (K slice, tile) order gives each XCD a contiguous run, walked in groups of GROUP_M
+// token tiles, so the workgroups resident on one XCD share A and B tiles in its L2
+// and a K slice of the activations is fetched by one XCD only.
 #include "device_common.h"
 #include "internal.h"
 #include "smlp.h"
@@ -67,14 +68,21 @@ __device__ __forceinline__ void put_h(void* base, int M, int N, int m, int n, fl
 // Swizzle of the 16-byte chunks within tile row r.
 __device__ __forceinline__ int chunk_swz(int r) { return (r >> 1) & 7; }
 
-// Workgroup index -> (tile_m, tile_n): XCD-contiguous runs of the tile order, which
-// walks GROUP_M token tiles down each column of weight tiles before moving right.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Workgroup -> (K slice, tile_m, tile_n).  Workgroups are dispatched in grid order
+// (x fastest) round-robin over the XCDs; the flattened (slice, tile) order is cut into
+// one contiguous run per XCD, so an XCD holds whole K slices (the activation slice is
+// fetched into one L2 only) and, within a slice, walks GROUP_M token tiles down each
+// column of weight tiles before moving right.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn, int& slice) {
   const int tiles = tiles_m * tiles_n;
-  const int per = tiles / XCDS, rem = tiles % XCDS;
-  const int xcd = bid % XCDS, idx = bid / XCDS;
+  const int total = tiles * gridDim.y;
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int per = total / XCDS, rem = total % XCDS;
+  const int xcd = lin % XCDS, idx = lin / XCDS;
   // XCD x owns the run starting at x*per + min(x, rem), of length per + (x < rem).
-  const int t = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int f = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  slice = f / tiles;
+  const int t = f - slice * tiles;
   const int group = GROUP_M * tiles_n;
   const int gi = t / group;
   const int first = gi * GROUP_M;
@@ -125,10 +133,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  int tile_m, tile_n;
-  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tile_m, tile_n);
+  int tile_m, tile_n, slice;
+  tile_coords(g.tiles_m, g.tiles_n, tile_m, tile_n, slice);
   const int K = g.K;
-  const int kbeg = blockIdx.y * g.kslice;
+  const int kbeg = slice * g.kslice;
   const int kend = min(K, kbeg + g.kslice);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
           if (f >= g.N) continue;
           const float gate = acc[i][j][e], up = acc[i][j + TN / 2][e];
           if (split) {
-            float* row = g.part + ((size_t)blockIdx.y * g.M + m) * (size_t)(2 * g.N);
+            float* row = g.part + ((size_t)slice * g.M + m) * (size_t)(2 * g.N);
             row[f] = gate;
             row[g.N + f] = up;
           } else {
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
           if (n >= g.N) continue;
           const float v = acc[i][j][e];
           if (split)
-            g.part[((size_t)blockIdx.y * g.M + m) * (size_t)g.N + n] = v;
+            g.part[((size_t)slice * g.M + m) * (size_t)g.N + n] = v;
           else if (g.out_f32)
             reinterpret_cast<float*>(g.out)[(size_t)m * g.N + n] = v;
           else

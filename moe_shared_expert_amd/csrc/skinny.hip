@@ -473,23 +473,54 @@ template <bool GU>
 __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__ part,
                                                        int ksplit, int M, int N, void* out,
                                                        int out_f32, int h_planes) {
-  const int P = GU ? 2 : 1;
-  const size_t total = (size_t)M * N;
+  // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, four
+  // slices in flight at a time, summed in slice order.
+  constexpr int P = GU ? 2 : 1;
+  const int N4 = N >> 2;
+  const size_t total = (size_t)M * N4;
+  const size_t sstride = (size_t)M * P * N;  // floats per slice
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
-    const int m = (int)(e / N), n = (int)(e % N);
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < ksplit; ++s) {
-      const float* src = part + ((size_t)s * M + m) * (size_t)(P * N) + n;
-      g += src[0];
-      if (GU) u += src[N];
+    const int m = (int)(e / N4), n = (int)(e % N4) * 4;
+    const float* base = part + (size_t)m * P * N + n;
+    f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= ksplit; s += 4) {
+      f32x4 a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride);
+        if (GU) b[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride + N);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        g += a[q];
+        if (GU) u += b[q];
+      }
     }
-    if (GU)
-      store_h(out, M, N, m, n, silu_mul(g, u), h_planes);
-    else if (out_f32)
-      reinterpret_cast<float*>(out)[e] = g;
-    else
-      reinterpret_cast<uint16_t*>(out)[e] = (uint16_t)f2bf(g);
+    for (; s < ksplit; ++s) {
+      g += *reinterpret_cast<const f32x4*>(base + (size_t)s * sstride);
+      if (GU) u += *reinterpret_cast<const f32x4*>(base + (size_t)s * sstride + N);
+    }
+    const size_t o = (size_t)m * N + n;
+    if (GU) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float h = silu_mul(g[j], u[j]);
+        hi[j] = f2bf(h);
+        lo[j] = f2bf(h - __uint_as_float(hi[j] << 16));
+      }
+      uint16_t* hp = reinterpret_cast<uint16_t*>(out);
+      *reinterpret_cast<u32x2*>(hp + o) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      if (h_planes == 2)
+        *reinterpret_cast<u32x2*>(hp + (size_t)M * N + o) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    } else if (out_f32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = g;
+    } else {
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + o) =
+          u32x2{f2bf(g[0]) | (f2bf(g[1]) << 16), f2bf(g[2]) | (f2bf(g[3]) << 16)};
+    }
   }
 }
 
@@ -552,9 +583,10 @@ static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
 
 int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int out_f32,
                     int h_planes, hipStream_t s) {
-  const size_t total = (size_t)M * N;
+  if (N % 4 != 0) return (int)hipErrorInvalidValue;  // bf16 shapes have N % 8 == 0
+  const size_t total = (size_t)M * (N / 4);
   int blocks = (int)((total + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 2048) blocks = 2048;
   if (gu)
     hipLaunchKernelGGL(skinny_finalize<true>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
                        out, out_f32, h_planes);
