@@ -22,7 +22,7 @@ extern "C" {
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit);
 
 /* The LDS-tiled (large-M) stages: tile of bm tokens x bn weight rows (0 and 0 =
- * automatic; bm in {128, 256}, bn in {64, 128, 256}), the wave grid wm x wn over the
+ * automatic; bm in {128, 256}, bn in {32 (down only), 64, 128, 256}), the wave grid wm x wn over the
  * tile (0 and 0 = automatic; each in {1, 2, 4}), the number of LDS stages ns (0 =
  * automatic, <= 8), the K split over workgroups (0 = automatic, <= 1024) and the
  * schedule (0 = automatic, 1 = plain, 2 = ping-pong: two wave groups half a K step

@@ -158,7 +158,8 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
 // LDS-tiled GEMM stage plan (measured on MI355X over M = 64 .. 8192, I = 768 and 6144):
 // 256 x 256 tiles (8 waves, 128 x 64 per wave) when they fill the chip at least twice
 // over and K is long; otherwise 128 x 128 tiles (4 waves) when they fill the chip
-// (gate_up) or fill it twice (down); else 128 x 64 tiles with a K split.
+// (gate_up) or fill it twice (down); down with a short K and few tiles: 128 x 32 tiles
+// without a K split; else 128 x 64 tiles with a K split.
 // Two LDS stages, so that two workgroups share a compute unit, and a K split over
 // workgroups when the tiles alone leave compute units idle.  N counts gate_up features
 // (two weight rows each) or down rows.  Returns false if a pinned tile is not compiled.
@@ -176,6 +177,11 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs)) {
     gp.bm = 128;
     gp.bn = 128;
+  } else if (stage == 1 && !hilo && K < 2048 && tiles_for(128, 64) < kCUs) {
+    // Down with a short K (the I of a TP shard): 32-row tiles fill the chip without a K
+    // split, so no fp32 partials and no finalize pass (half the time at M = 128).
+    gp.bm = 128;
+    gp.bn = 32;
   } else {
     gp.bm = 128;
     gp.bn = 64;
@@ -186,7 +192,7 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (gp.bm == 256) {
     gp.wm = 2;
     gp.wn = 4;
-  } else if (gp.bn == 64) {
+  } else if (gp.bn <= 64) {
     gp.wm = 4;
     gp.wn = 1;
   } else {
@@ -198,9 +204,9 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else {
     // Two stages where compiled (the two-plane 128 x 128 down tile has three).
     gp.ns = 2;
-    while (gp.ns < 4 && !smlp::gemm_instantiated(hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) ++gp.ns;
+    while (gp.ns < 4 && !smlp::gemm_instantiated(stage, hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) ++gp.ns;
   }
-  if (!smlp::gemm_instantiated(hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) return false;
+  if (!smlp::gemm_instantiated(stage, hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) return false;
   // The ping-pong schedule for the 256 x 256 gate_up tile (measured 6-9% faster there;
   // no faster for down).
   gp.sched = o.sched.load() ? o.sched.load()
@@ -215,7 +221,9 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   const int64_t ksteps = (K + 63) / 64;
   int64_t ks = o.ksplit.load();
   if (!ks) {
-    if (gp.bn == 64 && gp.bm == 128) {
+    if (gp.bn == 32) {
+      ks = 1;
+    } else if (gp.bn == 64 && gp.bm == 128) {
       // Few weight tiles (medium M): split K until about 3 (gate_up) or 1.75 (down)
       // workgroups per compute unit stream weights; fp32 partials cost 2 M / K of the
       // weight traffic per slice, so short K (I of a TP shard) takes at most 3 slices.
@@ -491,7 +499,7 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
 
 int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit, int sched) {
   if (stage < 0 || stage > 1 || !(bm == 0 || bm == 128 || bm == 256) ||
-      !(bn == 0 || bn == 64 || bn == 128 || bn == 256) || (bm == 0) != (bn == 0) ||
+      !(bn == 0 || bn == 32 || bn == 64 || bn == 128 || bn == 256) || (bm == 0) != (bn == 0) ||
       !(wm == 0 || wm == 1 || wm == 2 || wm == 4) || !(wn == 0 || wn == 1 || wn == 2 || wn == 4) ||
       (wm == 0) != (wn == 0) || ns < 0 || ns > 8 || ksplit < 0 || ksplit > 1024 || sched < 0 || sched > 2)
     return fail(SMLP_ERR_ARG, "bad large-M tuning (stage %d bm %d bn %d wm %d wn %d ns %d ksplit %d sched %d)",

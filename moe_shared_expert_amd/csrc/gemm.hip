@@ -509,6 +509,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GArgs g) {
 #define SMLP_GEMM_CONFIGS(X)                                                                    \
   X(256, 256, 2, 4, 2) X(128, 256, 2, 4, 3) X(128, 256, 2, 2, 3) X(128, 128, 2, 2, 2)           \
   X(128, 128, 2, 2, 4) X(128, 128, 4, 2, 4) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4) X(128, 64, 4, 1, 6)
+// Down only (one MFMA tile column per wave cannot pair gate and up rows).
+#define SMLP_GEMM_DN_CONFIGS(X) X(128, 32, 4, 1, 2) X(128, 32, 4, 1, 4)
 #define SMLP_GEMM_HILO_CONFIGS(X) X(128, 128, 2, 2, 3) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4)
 
 template <int MODE>
@@ -529,6 +531,9 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
       return (int)hipGetLastError();
     }
     SMLP_GEMM_CONFIGS(SMLP_G)
+    if constexpr (MODE == GM_DOWN_BF16) {
+      SMLP_GEMM_DN_CONFIGS(SMLP_G)
+    }
   }
 #undef SMLP_G
   return (int)hipErrorInvalidConfiguration;
@@ -536,13 +541,16 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool gemm_instantiated(bool hilo, int bm, int bn, int wm, int wn, int ns) {
+bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns) {
 #define SMLP_GM(BM_, BN_, WM_, WN_, NS_) \
   if (bm == BM_ && bn == BN_ && wm == WM_ && wn == WN_ && ns == NS_) return true;
-  if (hilo) {
+  if (stage == 1 && hilo) {
     SMLP_GEMM_HILO_CONFIGS(SMLP_GM)
   } else {
     SMLP_GEMM_CONFIGS(SMLP_GM)
+    if (stage == 1) {
+      SMLP_GEMM_DN_CONFIGS(SMLP_GM)
+    }
   }
 #undef SMLP_GM
   return false;

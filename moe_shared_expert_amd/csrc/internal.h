@@ -64,7 +64,7 @@ int launch_finalize(bool gate_up, const float* part, int ksplit, int M, int N, v
 // LDS-tiled GEMM stages (gemm.hip).  The ping-pong schedule exists for the 256 x 256,
 // 2 x 4 wave, two-stage tile of one activation plane.
 enum { GEMM_PLAIN = 1, GEMM_PINGPONG = 2 };
-bool gemm_instantiated(bool hilo, int bm, int bn, int wm, int wn, int ns);
+bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns);  // stage 0: gate_up, 1: down
 int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s);
 int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
 

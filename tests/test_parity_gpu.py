@@ -367,3 +367,36 @@ def test_gemm_pingpong_matches_plain(M, Hh, Ii):
     rows = np.array(sorted(set([0, 1, 255, 256, M - 1] + list(range(2, M, max(1, M // 40))))))
     ref = oracle.swiglu_mlp(f64(x[rows]), f64(wgu), f64(wd))
     assert_rms_close(outs[1][torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"ping-pong M={M}")
+
+
+# ------------------------------------------------------------------ graph replays
+@pytest.mark.parametrize("M,partial", [(16, False), (128, True), (512, False), (4096, False)])
+def test_graph_replays_match_eager(M, partial):
+    """A forward captured in a hipGraph, replayed several times with eager work (garbage
+    written over the output and the workspace) between replays, reproduces the eager
+    result bit for bit on every replay (small path, split-K path, large path,
+    ping-pong tile)."""
+    Hh, Ii = (2048, 1536) if M < 4096 else (1032, 2048)
+    x = synth.activations(M, Hh, config=15, copy=M).to(DEV)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=15)
+    wgu, wd = wgu.to(DEV), wd.to(DEV)
+    eager = run_forward(x, wgu, wd, partial)
+    out = torch.empty_like(eager)
+    ws = workspace_for(M, Hh, Ii, binding.SMLP_BF16)
+    side = torch.cuda.Stream(DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        binding.shared_mlp_forward(x, wgu, wd, out, partial_fp32=partial, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            binding.shared_mlp_forward(x, wgu, wd, out, partial_fp32=partial, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    ibits = torch.int32 if eager.dtype == torch.float32 else torch.int16
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0x7f)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(ibits), eager.view(ibits)), f"replay {rep}"
