@@ -42,12 +42,16 @@ WORKLOADS = {
                        "TP8 per-rank shard, M=128, H=7168, I_r=768, fp32 partial out, 16 copies cycled"),
     "prefill_rep_m8192": (8192, I, False, 2, 5,
                           "replicated prefill, M=8192, H=7168, I=6144, bf16 out, 2 copies cycled"),
+    "tp16_stack92_m128": (128, 384, True, 92, 4,
+                          "TP16 per-rank shard, 92 distinct layers, M=128, H=7168, I_r=384, fp32 partial out; "
+                          "chained through a per-token RMS rescale to bf16 (timed separately)"),
 }
 
 
 # Roofline bound of the dominant kernel per workload: weight streaming is HBM-bound;
 # at M = 8192 the gate_up GEMM does 2*M flops per weight byte and is MFMA-bound.
-BOUND = {"decode_rep_m16": "hbm", "tp8_shard_m128": "hbm", "prefill_rep_m8192": "mfma"}
+BOUND = {"decode_rep_m16": "hbm", "tp8_shard_m128": "hbm", "prefill_rep_m8192": "mfma",
+         "tp16_stack92_m128": "hbm"}
 
 
 def _ev():
@@ -135,6 +139,30 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
     torch.cuda.synchronize()
     gu_us = 1e3 * t0.elapsed_time(t1) / (gu_reps * copies)
 
+    chain_us = None
+    if name == "tp16_stack92_m128":
+        # the chained stack: layer l's fp32 partial, rescaled per token to unit RMS in
+        # bf16, is layer l + 1's input (one graph replay = the 92 layers)
+        xs = [torch.empty(M, H, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        xs[0].copy_(x)
+        chain = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(chain, stream=stream):
+                for i in range(copies):
+                    g, d = weights[i]
+                    binding.shared_mlp_forward(xs[i & 1], g, d, out, partial, ws, stream)
+                    binding.shared_mlp_rms_rescale(out, xs[(i + 1) & 1], stream)
+        torch.cuda.synchronize()
+        chain_reps = max(1, steps // copies)
+        with torch.cuda.stream(stream):
+            chain.replay()
+            t0.record(stream)
+            for _ in range(chain_reps):
+                chain.replay()
+            t1.record(stream)
+        torch.cuda.synchronize()
+        chain_us = 1e3 * t0.elapsed_time(t1) / (chain_reps * copies)
+
     out_elem = 4 if partial else 2
     alg = roofline.algorithmic_bytes(M, H, I_r, 2, out_elem)
     fl = roofline.flops(M, H, I_r)
@@ -147,6 +175,7 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
         "gbs": alg / (ms * 1e-3) / 1e9, "tflops": fl / (ms * 1e-3) / 1e12, "plan": plan,
         "gate_up_us": gu_us, "gate_up_alg_bytes": gu_alg, "gate_up_gbs": gu_alg / (gu_us * 1e-6) / 1e9,
         "gate_up_flops": 4 * M * H * I_r, "gate_up_tflops": 4 * M * H * I_r / (gu_us * 1e-6) / 1e12,
+        "chain_us_per_layer": chain_us,
     }
 
 
@@ -266,6 +295,8 @@ def main():
         "tflops": round(r["tflops"], 2),
         "roofline": roofline_entry(args.workload, r),
     }
+    if r["chain_us_per_layer"] is not None:
+        line["chain_us_per_layer"] = round(r["chain_us_per_layer"], 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

@@ -130,8 +130,55 @@ __global__ __launch_bounds__(256) void rms_rescale_kernel(const float* __restric
   }
 }
 
+// Rows of up to 8192 elements: the row is held in registers (one 16-byte load per thread
+// per 2048 elements, all in flight at once), reduced in a fixed order (per thread,
+// across the wave, across the 8 waves), then scaled and stored from the registers.
+template <int VPT>
+__global__ __launch_bounds__(512) void rms_rescale_reg_kernel(const float* __restrict__ in,
+                                                              uint16_t* __restrict__ out, int H) {
+  const int m = blockIdx.x;
+  const float4* row = reinterpret_cast<const float4*>(in + (size_t)m * H);
+  const int nv = H / 4;
+  float4 q[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = threadIdx.x + i * 512;
+    q[i] = v < nv ? row[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    ss = fmaf(q[i].x, q[i].x, ss);
+    ss = fmaf(q[i].y, q[i].y, ss);
+    ss = fmaf(q[i].z, q[i].z, ss);
+    ss = fmaf(q[i].w, q[i].w, ss);
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  __shared__ float part[8];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) total += part[w];
+  const float scale = 1.0f / sqrtf(total / (float)H);
+  u32x2* orow = reinterpret_cast<u32x2*>(out + (size_t)m * H);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = threadIdx.x + i * 512;
+    if (v < nv)
+      orow[v] = u32x2{pack_bf2(q[i].x * scale, q[i].y * scale), pack_bf2(q[i].z * scale, q[i].w * scale)};
+  }
+}
+
 int launch_rms_rescale(const float* in, uint16_t* out, int64_t M, int64_t H, hipStream_t s) {
-  hipLaunchKernelGGL(rms_rescale_kernel, dim3((unsigned)M), dim3(256), 0, s, in, out, (int)H);
+  if (H <= 2048)
+    hipLaunchKernelGGL(rms_rescale_reg_kernel<1>, dim3((unsigned)M), dim3(512), 0, s, in, out, (int)H);
+  else if (H <= 4096)
+    hipLaunchKernelGGL(rms_rescale_reg_kernel<2>, dim3((unsigned)M), dim3(512), 0, s, in, out, (int)H);
+  else if (H <= 8192)
+    hipLaunchKernelGGL(rms_rescale_reg_kernel<4>, dim3((unsigned)M), dim3(512), 0, s, in, out, (int)H);
+  else
+    hipLaunchKernelGGL(rms_rescale_kernel, dim3((unsigned)M), dim3(256), 0, s, in, out, (int)H);
   return (int)hipGetLastError();
 }
 

@@ -167,11 +167,14 @@ def test_stack92_chain_properties(stack92):
         x = nxt
 
 
-def test_rms_rescale_against_oracle():
-    a = synth.normal((128, H), 0.3, seed=4242, dtype=torch.float32)
+@pytest.mark.parametrize("Hh", [H, 12, 2044, 4100, 8192, 9000])
+def test_rms_rescale_against_oracle(Hh):
+    # row lengths covering each register-resident variant, ragged tails and the two-pass
+    # fallback for rows longer than 8192
+    a = synth.normal((128, Hh), 0.3, seed=4242, dtype=torch.float32)
     a[5] *= 100.0
     a[7] *= 1e-3
-    out = torch.empty(128, H, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(128, Hh, dtype=torch.bfloat16, device=DEV)
     binding.shared_mlp_rms_rescale(a.to(DEV), out)
     torch.cuda.synchronize()
     ref = oracle.rms_rescale_rows(f64(a))
