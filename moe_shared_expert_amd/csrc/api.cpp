@@ -21,8 +21,8 @@ thread_local std::string g_last_error;
 constexpr int kCUs = 256;
 // The weight-streaming kernels handle up to 128 tokens per call.
 constexpr int64_t kSmallMaxM = 128;
-// Default M-dispatch threshold: on MI355X the LDS-staged weight-streaming kernel is
-// fastest up to 32 tokens and the LDS-tiled path from 33 on.
+// Default M-dispatch threshold: on MI355X the weight-streaming kernel is fastest up
+// to 32 tokens and the LDS-tiled path from 33 on.
 constexpr int64_t kDefaultLargeMMin = 33;
 constexpr int64_t kLimit = (int64_t)1 << 31;
 

@@ -131,8 +131,12 @@ __device__ __forceinline__ void finish_workgroup(const SkArgs& a,
     }
 }
 
-// Streaming kernel (M <= 32).  Same work split as the LDS-staged kernel, but each
-// operand block reaches a wave-private LDS ring by direct buffer-to-LDS loads: a
+// Streaming kernel (M <= 32).  A workgroup owns the contiguous feature range
+// [blockIdx.x * fpw, +fpw) and a K slice; the range is cut into NT 16-row MFMA tiles.
+// gate_up tiles pack 8 features: rows 0-7 are their gate rows and rows 8-15 their up
+// rows; down tiles are 16 consecutive rows.  The K slice is interleaved over the waves
+// in 64-element steps.  Each operand block reaches a wave-private LDS ring by direct
+// buffer-to-LDS loads: a
 // 16-byte load per lane fills 1 KB with 8 rows x 128 bytes (one 64-element K step),
 // lane p writing slot p, the lane choosing its global chunk so that slot s of row r
 // holds chunk (s % 8) ^ ((r / 2) % 8) and the 16-row fragment reads are free of bank
@@ -525,10 +529,10 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
 }
 
 // Instantiated configurations (MT, NB, WAVES, U) per kernel kind (MT = 16-token
-// tiles, NB = 16-feature blocks; U = register stages for the LDS-staged kind, the
-// unroll for the direct kind); none spills registers.
-// Streaming kind (MT, NB, WAVES, STAGES): LDS = WAVES x STAGES x (NB + activation
-// tiles) x 2 KB <= 160 KB, activation tiles = MT (gate_up) or 2 MT (down).
+// tiles; none spills registers).  Streaming kind: NB = 16-row MFMA tiles, U = ring
+// stages, LDS = WAVES x STAGES x (NB + activation tiles) x 2 KB <= 160 KB with
+// activation tiles = MT (gate_up) or 2 MT (down).  Direct kind: NB = 16-feature
+// blocks, U = 64-element K steps per wave per pipeline stage.
 #define SMLP_SK_GU_STREAM16(X)                                                                 \
   X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 2, 4, 4) X(1, 2, 8, 3) X(1, 3, 4, 3) X(1, 3, 4, 4)          \
   X(1, 3, 4, 5) X(1, 3, 8, 2) X(1, 4, 4, 4) X(2, 1, 4, 4) X(2, 2, 4, 4) X(2, 3, 4, 3)          \
