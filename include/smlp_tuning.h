@@ -22,14 +22,12 @@ extern "C" {
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit);
 
 /* The LDS-tiled (large-M) stages: tile of bm tokens x bn weight rows (0 and 0 =
- * automatic; bm in {128, 256}, bn in {32 (down only), 64, 128, 256}), the wave grid wm x wn over the
- * tile (0 and 0 = automatic; each in {1, 2, 4}), the number of LDS stages ns (0 =
- * automatic, <= 8), the K split over workgroups (0 = automatic, <= 1024) and the
- * schedule (0 = automatic, 1 = plain, 2 = ping-pong: two wave groups half a K step
- * apart, only for the 256 x 256, 2 x 4 wave, two-stage tile).  Returns SMLP_OK or
- * SMLP_ERR_ARG; a pinned combination that is not compiled makes later plans fail with
- * SMLP_ERR_ARG. */
-int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit, int sched);
+ * automatic; bm in {128, 256}, bn in {32 (down only), 64, 128, 256}), the wave grid
+ * wm x wn over the tile (0 and 0 = automatic; each in {1, 2, 4}), the number of LDS
+ * stages ns (0 = automatic, <= 8) and the K split over workgroups (0 = automatic,
+ * <= 1024).  Returns SMLP_OK or SMLP_ERR_ARG; a pinned combination that is not compiled
+ * makes later plans fail with SMLP_ERR_ARG. */
+int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit);
 
 #ifdef __cplusplus
 }

@@ -58,7 +58,7 @@ EXPORTS = {
 # declared in include/smlp_tuning.h
 TUNING_EXPORTS = {
     "shared_mlp_tune_skinny": (_int, [_int, _int, _int, _int, _int, _int]),
-    "shared_mlp_tune_gemm": (_int, [_int, _int, _int, _int, _int, _int, _int, _int]),
+    "shared_mlp_tune_gemm": (_int, [_int, _int, _int, _int, _int, _int, _int]),
 }
 
 
@@ -189,9 +189,9 @@ def shared_mlp_tune_skinny(stage: int, kind: int = 0, nb: int = 0, waves: int = 
 
 
 def shared_mlp_tune_gemm(stage: int, bm: int = 0, bn: int = 0, wm: int = 0, wn: int = 0, ns: int = 0,
-                         ksplit: int = 0, sched: int = 0):
+                         ksplit: int = 0):
     """Pin large-M tile parameters (0 = automatic); see include/smlp_tuning.h."""
-    _check(lib().shared_mlp_tune_gemm(stage, bm, bn, wm, wn, ns, ksplit, sched))
+    _check(lib().shared_mlp_tune_gemm(stage, bm, bn, wm, wn, ns, ksplit))
 
 
 def forward(x, w_gate_up, w_down, partial_fp32=False, workspace=None, stream=None):

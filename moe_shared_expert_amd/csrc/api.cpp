@@ -69,7 +69,7 @@ struct SkinnyOverride {
 SkinnyOverride g_tune[2];
 
 struct GemmOverride {
-  std::atomic<int> bm{0}, bn{0}, wm{0}, wn{0}, ns{0}, ksplit{0}, sched{0};
+  std::atomic<int> bm{0}, bn{0}, wm{0}, wn{0}, ns{0}, ksplit{0};
 };
 GemmOverride g_gtune[2];
 
@@ -207,14 +207,6 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     while (gp.ns < 4 && !smlp::gemm_instantiated(stage, hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) ++gp.ns;
   }
   if (!smlp::gemm_instantiated(stage, hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns)) return false;
-  // The ping-pong schedule for the 256 x 256 gate_up tile (measured 6-9% faster there;
-  // no faster for down).
-  gp.sched = o.sched.load() ? o.sched.load()
-                            : (stage == 0 && !hilo && gp.bm == 256 && gp.bn == 256 && gp.wm == 2 && gp.wn == 4 && gp.ns == 2)
-                                  ? smlp::GEMM_PINGPONG
-                                  : smlp::GEMM_PLAIN;
-  if (gp.sched == smlp::GEMM_PINGPONG && (hilo || gp.bm != 256 || gp.bn != 256 || gp.wm != 2 || gp.wn != 4 || gp.ns != 2))
-    return false;
   gp.tiles_m = (int)((M + gp.bm - 1) / gp.bm);
   const int64_t tiles = tiles_for(gp.bm, gp.bn);
   gp.tiles = (int)tiles;
@@ -497,20 +489,19 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
   return ok();
 }
 
-int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit, int sched) {
+int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit) {
   if (stage < 0 || stage > 1 || !(bm == 0 || bm == 128 || bm == 256) ||
       !(bn == 0 || bn == 32 || bn == 64 || bn == 128 || bn == 256) || (bm == 0) != (bn == 0) ||
       !(wm == 0 || wm == 1 || wm == 2 || wm == 4) || !(wn == 0 || wn == 1 || wn == 2 || wn == 4) ||
-      (wm == 0) != (wn == 0) || ns < 0 || ns > 8 || ksplit < 0 || ksplit > 1024 || sched < 0 || sched > 2)
-    return fail(SMLP_ERR_ARG, "bad large-M tuning (stage %d bm %d bn %d wm %d wn %d ns %d ksplit %d sched %d)",
-                stage, bm, bn, wm, wn, ns, ksplit, sched);
+      (wm == 0) != (wn == 0) || ns < 0 || ns > 8 || ksplit < 0 || ksplit > 1024)
+    return fail(SMLP_ERR_ARG, "bad large-M tuning (stage %d bm %d bn %d wm %d wn %d ns %d ksplit %d)", stage,
+                bm, bn, wm, wn, ns, ksplit);
   g_gtune[stage].bm = bm;
   g_gtune[stage].bn = bn;
   g_gtune[stage].wm = wm;
   g_gtune[stage].wn = wn;
   g_gtune[stage].ns = ns;
   g_gtune[stage].ksplit = ksplit;
-  g_gtune[stage].sched = sched;
   return ok();
 }
 

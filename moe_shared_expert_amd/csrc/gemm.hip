@@ -96,7 +96,7 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
 // semantics would wait for every load in flight, the later steps' LDS loads included.
 // The LDS reads of a step are all consumed by its MFMAs (so complete) before the
 // barrier; the empty asm statements keep the compiler from moving memory accesses
-// across it, and the scheduling barriers keep the MFMAs of a phase on their side.
+// across it, and the scheduling barriers keep the multiplies of a step on their side.
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -301,208 +301,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
     }
 }
 
-// Ping-pong schedule for 256 x 256 tiles.  The 8 waves form two groups of four (one
-// wave of each group per SIMD); group g owns tile rows [128 g, 128 g + 128) and wave w
-// of a group the 64 columns [64 w, 64 w + 64), i.e. 4 x 2 MFMA tiles of 32 x 32.  The
-// groups run half a K step apart: in every phase one group multiplies a whole K step
-// from fragments already in its registers while the other group reads the fragments
-// of its next half step from LDS, so each SIMD always has a wave ready to issue MFMAs (in
-// the plain schedule both waves of a SIMD hit the same barrier and read LDS at the
-// same time).  Phases are half K steps (fragments of a whole step would not fit next
-// to the 128 accumulators), four barriers per K step; two LDS stages; loads for step
-// k + 2 are issued after the barrier that frees stage k % 2.
-template <int MODE>
-__global__ __launch_bounds__(512) void gemm_pp_kernel(GArgs g) {
-  constexpr bool GU = MODE == GM_GATE_UP;
-  constexpr int BM = 256, BN = 256, W = 8, TM = 4, TN = 2, NS = 2;
-  constexpr int AL = BM / 8 / W, BL = BN / 8 / W;  // 1 KB block loads per wave per step
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  static_assert(MODE != GM_DOWN_HILO, "one activation plane");
-  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // 0: rows 0-127, 1: rows 128-255
-  const int wm = grp, wn = wave & 3;
-  int tile_m, tile_n, slice;
-  tile_coords(g.tiles_m, g.tiles_n, tile_m, tile_n, slice);
-  const int K = g.K;
-  const int kbeg = slice * g.kslice;
-  const int kend = min(K, kbeg + g.kslice);
-  const int nk = (kend - kbeg + BK - 1) / BK;
-
-  const uint32_t abytes = (uint32_t)g.M * (uint32_t)K * 2u;
-  const uint32_t bbytes = (uint32_t)g.b_rows * (uint32_t)K * 2u;
-  const __amdgpu_buffer_rsrc_t arsc = make_rsrc(g.a, abytes);
-  const __amdgpu_buffer_rsrc_t brsc = make_rsrc(g.b, bbytes);
-
-  const int prow = lane >> 3;
-  uint32_t aoff[AL], boff[BL];
-  int achk[AL], bchk[BL];
-#pragma unroll
-  for (int i = 0; i < AL; ++i) {
-    const int r = (i * W + wave) * 8 + prow;
-    achk[i] = (lane & 7) ^ chunk_swz(r);
-    const int m = tile_m * BM + r;
-    aoff[i] = m < g.M ? (uint32_t)m * (uint32_t)K * 2u + achk[i] * 16 : abytes;
-  }
-#pragma unroll
-  for (int i = 0; i < BL; ++i) {
-    const int r = (i * W + wave) * 8 + prow;
-    bchk[i] = (lane & 7) ^ chunk_swz(r);
-    int row;
-    bool ok;
-    if (GU) {
-      // Each wave column's 64 rows: 32 gate rows, then the matching up rows.
-      const int wc = r / 64, rr = r % 64;
-      const int f = tile_n * (BN / 2) + wc * 32 + rr % 32;
-      ok = f < g.N;
-      row = rr < 32 ? f : g.up_off + f;
-    } else {
-      row = tile_n * BN + r;
-      ok = row < g.N;
-    }
-    boff[i] = ok ? (uint32_t)row * (uint32_t)K * 2u + bchk[i] * 16 : bbytes;
-  }
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  auto issue = [&](int buf, int k0) {
-    char* st = lds + buf * STAGE;
-    const uint32_t kb = (uint32_t)k0 * 2u;
-#pragma unroll
-    for (int i = 0; i < AL; ++i) {
-      const bool ok = aoff[i] != abytes && k0 + achk[i] * 8 < kend;
-      buf_ld_lds(arsc, st + (i * W + wave) * 1024, ok ? aoff[i] + kb : abytes);
-    }
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      const bool ok = boff[i] != bbytes && k0 + bchk[i] * 8 < kend;
-      buf_ld_lds(brsc, st + A_BYTES + (i * W + wave) * 1024, ok ? boff[i] + kb : bbytes);
-    }
-  };
-
-  // Fragments of one half K step (2 sub-steps of 16) for this wave.
-  const int fr = lane & 31, fh = lane >> 5;
-  const int fsw = chunk_swz(fr);
-  u32x4 fa[2][TM], fb[2][TN];
-  auto read_half = [&](int hs) {  // half step hs: stage (hs / 2) % 2, sub-steps 2 (hs % 2) + {0, 1}
-    const char* st = lds + ((hs >> 1) & 1) * STAGE;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int ks = 2 * (hs & 1) + q;
-      const int coff = ((2 * ks + fh) ^ fsw) * 16;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[q][i] = *reinterpret_cast<const u32x4*>(st + ((wm * TM + i) * 32 + fr) * 128 + coff);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[q][j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + ((wn * TN + j) * 32 + fr) * 128 + coff);
-    }
-  };
-  auto mfma_half = [&]() {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[q][i], fb[q][j], acc[i][j]);
-  };
-  auto lds_done = [&]() { __builtin_amdgcn_s_waitcnt(0xc07f); };  // lgkmcnt(0)
-
-  // Half steps h = 0 .. 2 nk - 1.  Phase X_h: group 0 multiplies h, group 1 reads h;
-  // phase Y_h: group 0 reads h + 1, group 1 multiplies h.  Step k = h / 2 lives in
-  // stage k % 2; its loads must have landed before group 0 reads half 2k (at the end
-  // of X_{2k-1}), and stage k % 2 is reloaded with step k + 2 once group 1 has read
-  // half 2k + 1 (after X_{2k+1}).
-  // Each group runs its own copy of the loop, so that every accumulator update is
-  // unconditional; both copies reach the same barriers in the same order.  Half steps
-  // h = 0 .. 2 nk - 1; step k = h / 2 lives in stage k % 2.  Phase X_h: group 0
-  // multiplies h, group 1 reads h; phase Y_h: group 0 reads h + 1, group 1 multiplies
-  // h.  At the end of X_{2k+1} both groups have read step k (group 0 in Y_{2k-1} and
-  // Y_{2k}, group 1 in X_{2k} and X_{2k+1}) and the loads of step k + 1 have landed;
-  // after that barrier stage k % 2 is reloaded with step k + 2.
-  const int nh = 2 * nk;
-  auto after_x = [&](int h) {  // end of phase X_h, start of phase Y_h
-    lds_done();
-    if (h & 1) wait_vmcnt<0>();  // step h / 2 + 1 has landed
-    block_barrier();
-    if ((h & 1) && (h >> 1) + 2 < nk) issue((h >> 1) & 1, kbeg + ((h >> 1) + 2) * BK);
-  };
-  auto after_y = [&]() {
-    lds_done();
-    block_barrier();
-  };
-  if (nk > 0) {
-    issue(0, kbeg);
-    wait_vmcnt<0>();
-    block_barrier();
-    if (nk > 1) issue(1, kbeg + BK);
-    if (grp == 0) {
-      read_half(0);
-      after_y();
-      for (int h = 0; h < nh; ++h) {
-        mfma_half();
-        after_x(h);
-        if (h + 1 < nh) read_half(h + 1);
-        after_y();
-      }
-    } else {
-      after_y();
-      for (int h = 0; h < nh; ++h) {
-        read_half(h);
-        after_x(h);
-        mfma_half();
-        after_y();
-      }
-    }
-  }
-
-  // Epilogue (as the plain kernel, with this kernel's wave grid).
-  const bool split = gridDim.y > 1;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int m = tile_m * BM + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-      if (m >= g.M) continue;
-      if (GU) {
-        const int f = tile_n * (BN / 2) + wn * 32 + fr;
-        if (f >= g.N) continue;
-        const float gate = acc[i][0][e], up = acc[i][1][e];
-        if (split) {
-          float* row = g.part + ((size_t)slice * g.M + m) * (size_t)(2 * g.N);
-          row[f] = gate;
-          row[g.N + f] = up;
-        } else {
-          put_h(g.out, g.M, g.N, m, f, silu_mul(gate, up), g.h_planes);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int n = tile_n * BN + (wn * TN + j) * 32 + fr;
-          if (n >= g.N) continue;
-          const float v = acc[i][j][e];
-          if (split)
-            g.part[((size_t)slice * g.M + m) * (size_t)g.N + n] = v;
-          else if (g.out_f32)
-            reinterpret_cast<float*>(g.out)[(size_t)m * g.N + n] = v;
-          else
-            reinterpret_cast<uint16_t*>(g.out)[(size_t)m * g.N + n] = (uint16_t)f2bf(v);
-        }
-      }
-    }
-}
-
 // Tile configurations (BM, BN, WM, WN, stages).  LDS holds stages x (BM + BN) x 128
 // bytes (the two-plane down mode: stages x (2 BM + BN) x 128) of the 160 KB per
 // workgroup.
@@ -524,12 +322,6 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
   if constexpr (MODE == GM_DOWN_HILO) {
     SMLP_GEMM_HILO_CONFIGS(SMLP_G)
   } else {
-    if (gp.sched == GEMM_PINGPONG) {
-      if (gp.bm != 256 || gp.bn != 256 || gp.wm != 2 || gp.wn != 4 || gp.ns != 2)
-        return (int)hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((gemm_pp_kernel<MODE>), grid, dim3(512), 0, s, a);
-      return (int)hipGetLastError();
-    }
     SMLP_GEMM_CONFIGS(SMLP_G)
     if constexpr (MODE == GM_DOWN_BF16) {
       SMLP_GEMM_DN_CONFIGS(SMLP_G)

@@ -29,7 +29,6 @@ struct GemmPlan {
   int bm, bn;    // tile: tokens x weight rows (gate_up: bn/2 features)
   int wm, wn;    // wave grid
   int ns;        // LDS stages
-  int sched;     // GEMM_PLAIN or GEMM_PINGPONG
   int tiles_m;   // tiles along M (tiles = tiles_m * tiles along N)
   int tiles;
   int ksplit;    // workgroups along K
@@ -61,9 +60,7 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
 int launch_finalize(bool gate_up, const float* part, int ksplit, int M, int N, void* out,
                     int out_f32, int h_planes, hipStream_t s);
 
-// LDS-tiled GEMM stages (gemm.hip).  The ping-pong schedule exists for the 256 x 256,
-// 2 x 4 wave, two-stage tile of one activation plane.
-enum { GEMM_PLAIN = 1, GEMM_PINGPONG = 2 };
+// LDS-tiled GEMM stages (gemm.hip).
 bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns);  // stage 0: gate_up, 1: down
 int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s);
 int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
