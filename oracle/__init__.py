@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for the shared-expert SwiGLU MLP (test infrastructure).
+"""CPU fp64 oracle for the shared-expert SwiGLU MLP and the sharded MLA latent
+projection (test infrastructure).
 
 This package is test infrastructure. Only ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import it; the product path (the
@@ -20,4 +21,12 @@ from .swiglu_mlp import (  # noqa: F401
     feature_concat_design,
     rms_rescale_rows,
     shard_sequence_parallel_mlp,
+)
+from .mla_latent import (  # noqa: F401
+    check_geometry,
+    linear,
+    merged_column_shard,
+    gather_rank_major,
+    restore_logical,
+    sharded_projection,
 )
