@@ -48,10 +48,24 @@ WORKLOADS = {
 }
 
 
+# Merged MLA latent projection (vLLM PR 345): name -> (M, tp, layers, description).  One
+# step is one rank's layer: its projection into its slot of the gathered output, then
+# the restore of the gathered output to the logical q_a / kv_a order.  Every (rank,
+# layer) shard is a distinct buffer (24 layers x 2112 x 7168 bf16 = 727 MB in total),
+# cycled, so the Infinity Cache cannot hold the weights.
+LATENT_WORKLOADS = {
+    "mla_latent_rep_m16": (16, 1, 24, "merged MLA latent q_a/kv_a projection, replicated (TP1), M=16, "
+                                      "K=7168, N=2112 (1536 + 576), bf16, 24 layers cycled"),
+    "mla_latent_tp16_m16": (16, 16, 24, "merged MLA latent q_a/kv_a projection, one TP16 rank, M=16, "
+                                        "K=7168, shard [132, 7168] projected into its slot of the gathered "
+                                        "[16, 2112] output, then restored to logical order; the shards of "
+                                        "all 16 ranks x 24 layers cycled"),
+}
+
 # Roofline bound of the dominant kernel per workload: weight streaming is HBM-bound;
 # at M = 8192 the gate_up GEMM does 2*M flops per weight byte and is MFMA-bound.
 BOUND = {"decode_rep_m16": "hbm", "tp8_shard_m128": "hbm", "prefill_rep_m8192": "mfma",
-         "tp16_stack92_m128": "hbm"}
+         "tp16_stack92_m128": "hbm", "mla_latent_rep_m16": "hbm", "mla_latent_tp16_m16": "hbm"}
 
 
 def _ev():
@@ -179,14 +193,156 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
     }
 
 
+def _graph_time_us(stream, fn, n, reps):
+    """Average duration of fn(i) for i in range(n), captured as one graph and replayed
+    `reps` times after one untimed replay (HIP events on the launch stream)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i, stream)
+    torch.cuda.synchronize()
+    t0, t1 = _ev(), _ev()
+    with torch.cuda.stream(stream):
+        g.replay()
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * t0.elapsed_time(t1) / (reps * n)
+
+
+def run_latent(name, steps, warmup, dev):
+    """Time `steps` rank-layer steps of the merged latent projection (value) and the
+    projection kernel alone (roofline)."""
+    M, tp, layers, desc = LATENT_WORKLOADS[name]
+    sizes = synth.LATENT_SIZES
+    n = sum(sizes)
+    n_r = n // tp
+    x = synth.activations(M, H, config=synth.LATENT_CONFIG).to(dev)
+    shards = []   # (rank, weight) for every layer and rank
+    for layer in range(layers):
+        w = synth.latent_weight(n, H, copy=layer)
+        for r in range(tp):
+            if tp == 1:
+                shards.append((0, w.to(dev)))
+                continue
+            rows, off = [], 0
+            for sz in sizes:   # rank r's piece of each range, in range order
+                p = sz // tp
+                rows.append(w[off + r * p: off + (r + 1) * p])
+                off += sz
+            shards.append((r, torch.cat(rows, 0).contiguous().to(dev)))
+        del w
+    copies = len(shards)
+    gathered = torch.empty(M, n, dtype=torch.bfloat16, device=dev)
+    logical = torch.empty_like(gathered)
+    wsb = binding.shared_mlp_linear_workspace_bytes(M, H, n_r)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    plan = binding.shared_mlp_linear_plan(M, H, n_r)
+
+    def proj(i, stream):
+        r, w = shards[i % copies]
+        binding.shared_mlp_linear(x, w, gathered[:, r * n_r:(r + 1) * n_r], ws, stream)
+
+    def step(i, stream):
+        proj(i, stream)
+        if tp > 1:
+            binding.shared_mlp_restore_logical(gathered, logical, sizes, tp, stream)
+
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, copies)):
+            step(i, stream)
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    step_us = _graph_time_us(stream, step, copies, reps)
+    proj_us = _graph_time_us(stream, proj, copies, reps)
+    restore_us = None
+    if tp > 1:
+        restore_us = _graph_time_us(
+            stream, lambda i, st: binding.shared_mlp_restore_logical(gathered, logical, sizes, tp, st), 64,
+            max(1, steps // 64))
+    proj_alg = roofline.latent_projection_bytes(M, H, n_r)
+    alg = proj_alg + (roofline.latent_restore_bytes(M, n) if tp > 1 else 0)
+    fl = 2 * M * H * n_r
+    return {
+        "name": name, "desc": desc, "M": M, "tp": tp, "n": n, "n_r": n_r, "copies": copies,
+        "steps": reps * copies, "ms_per_step": step_us * 1e-3, "us_per_layer": step_us,
+        "alg_bytes": alg, "gbs": alg / (step_us * 1e-6) / 1e9, "tflops": fl / (step_us * 1e-6) / 1e12,
+        "plan": plan, "proj_us": proj_us, "proj_alg_bytes": proj_alg,
+        "proj_gbs": proj_alg / (proj_us * 1e-6) / 1e9, "restore_us": restore_us,
+    }
+
+
+def latent_cpu_baseline(name, budget_s=12.0):
+    """The fp64 oracle (rank-local projection, and the restore for tp > 1) on host cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    M, tp, layers, desc = LATENT_WORKLOADS[name]
+    sizes = synth.LATENT_SIZES
+    n = sum(sizes)
+    x = synth.to_f64(synth.activations(M, H, config=synth.LATENT_CONFIG))
+    ws = [synth.to_f64(synth.latent_weight(n, H, copy=c)) for c in range(2)]
+    shards = [oracle.merged_column_shard(w, sizes, tp, 0) for w in ws]
+    gathered = oracle.linear(x, ws[0])   # stands in for the gathered rank outputs
+    oracle.linear(x[:1], shards[0])
+    k = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.linear(x, shards[k % 2])
+        if tp > 1:
+            oracle.restore_logical(gathered, sizes, tp)
+        k += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / k * (k + 1) > 3 * budget_s:
+            break
+    per = el / k
+    alg = roofline.latent_projection_bytes(M, H, n // tp) + (roofline.latent_restore_bytes(M, n) if tp > 1 else 0)
+    return {"value": alg / per / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{k} rank-layer steps of the {desc} workload (2 weight copies cycled), numpy fp64 "
+                      f"oracle, {per * 1e3:.2f} ms per step",
+            "seconds_per_layer": per, "cpu": platform.processor() or platform.machine()}
+
+
+def latent_line(args, r):
+    roof = {"bound": "hbm", "kernel": "merged latent projection (weight-streaming)",
+            "achieved": round(r["proj_gbs"], 1), "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["proj_gbs"] / roofline.HBM_PEAK_GBS, 4), "kernel_us": round(r["proj_us"], 3),
+            "bytes_per_launch": r["proj_alg_bytes"], "traffic": profiled_traffic(args.workload)}
+    line = {
+        "metric": METRIC, "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/7168) weights)",
+        "config": {"workload": r["desc"], "M": r["M"], "K": H, "N": r["n"], "tp": r["tp"],
+                   "N_rank": r["n_r"], "weight_buffers": r["copies"], "path": r["plan"]["path_name"],
+                   "launch": "hipGraph replay"},
+        "us_per_layer": round(r["us_per_layer"], 3),
+        "hbm_frac": round(r["gbs"] / roofline.HBM_PEAK_GBS, 4),
+        "roofline": roof,
+    }
+    if r["restore_us"] is not None:
+        line["restore_us"] = round(r["restore_us"], 3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = latent_cpu_baseline(args.workload)
+    return line
+
+
 KERNEL_SOURCES = ("moe_shared_expert_amd/csrc/skinny.hip", "moe_shared_expert_amd/csrc/gemm.hip",
                   "moe_shared_expert_amd/csrc/device_common.h", "moe_shared_expert_amd/csrc/api.cpp")
 
 
 def profiled_traffic(name):
-    """HBM bytes per launch of the gate_up kernel from the committed rocprofv3 counter
-    summary of this workload (profiles/<workload>.md), or None when that summary was
-    taken on different kernel sources than the ones built now."""
+    """HBM bytes per launch of the dominant kernel (gate_up, or the latent projection)
+    from the committed rocprofv3 counter summary of this workload
+    (profiles/<workload>.md), or None when that summary was taken on different kernel
+    sources than the ones built now."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"{name}.md")
@@ -197,7 +353,7 @@ def profiled_traffic(name):
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     m = re.search(r"kernel source hash[^`]*`([0-9a-f]+)`", text)
-    t = re.search(r"gate_up traffic bytes per launch: (\d+)", text)
+    t = re.search(r"(?:gate_up|projection) traffic bytes per launch: (\d+)", text)
     if not m or not t or m.group(1) != h.hexdigest()[:16]:
         return None
     return int(t.group(1))
@@ -255,7 +411,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode_rep_m16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode_rep_m16", choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also print the M sweep lines")
     ap.add_argument("--launch", default="graph", choices=("graph", "eager"),
@@ -279,6 +435,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 3}))
         return
     binding.lib()
+    if args.workload in LATENT_WORKLOADS:
+        print(json.dumps(latent_line(args, run_latent(args.workload, args.steps, args.warmup, dev))), flush=True)
+        return
     r = run_workload(args.workload, args.steps, args.warmup, dev, args.launch)
     line = {
         "metric": METRIC, "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1,

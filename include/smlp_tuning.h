@@ -16,12 +16,14 @@
 extern "C" {
 #endif
 
-/* stage: 0 = gate_up, 1 = down.  kind in {0,2,3}; nb in {0,1,2,4}; waves in {0,4,8};
- * u in {0,...,5}; 0 <= ksplit <= 1024.  Returns SMLP_OK or SMLP_ERR_ARG.  A pinned
- * combination that is not a compiled kernel makes later plans fail with SMLP_ERR_ARG. */
+/* stage: 0 = gate_up, 1 = down, 2 = the plain projection of smlp_latent.h (kind 3
+ * only).  kind in {0,2,3}; nb in {0,...,4}; waves in {0,4,8}; u in {0,...,8};
+ * 0 <= ksplit <= 1024.  Returns SMLP_OK or SMLP_ERR_ARG.  A pinned combination that is
+ * not a compiled kernel makes later plans fail with SMLP_ERR_ARG. */
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit);
 
-/* The LDS-tiled (large-M) stages: tile of bm tokens x bn weight rows (0 and 0 =
+/* The LDS-tiled (large-M) stages (stage 2: the plain projection, planned like down):
+ * tile of bm tokens x bn weight rows (0 and 0 =
  * automatic; bm in {128, 256}, bn in {32 (down only), 64, 128, 256}), the wave grid
  * wm x wn over the tile (0 and 0 = automatic; each in {1, 2, 4}), the number of LDS
  * stages ns (0 = automatic, <= 8) and the K split over workgroups (0 = automatic,

@@ -54,6 +54,12 @@ EXPORTS = {
     "shared_mlp_shard_eligible": (_int, [_int, _int, _int, _int, _i64, _i64]),
     "shared_mlp_slice_rank": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "shared_mlp_rms_rescale": (_int, [_vp, _vp, _i64, _i64, _vp]),
+    # declared in include/smlp_latent.h
+    "shared_mlp_linear_plan": (_int, [_i64, _i64, _i64, ctypes.POINTER(_Plan)]),
+    "shared_mlp_linear_workspace_bytes": (_int, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
+    "shared_mlp_linear": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
+    "shared_mlp_restore_logical": (_int, [_vp, _vp, _i64, _i64, ctypes.POINTER(_i64), _int, _int, _int,
+                                          _vp]),
 }
 # declared in include/smlp_tuning.h
 TUNING_EXPORTS = {
@@ -226,3 +232,52 @@ def shared_mlp_rms_rescale(inp, out, stream=None):
     if inp.dtype != torch.float32 or out.dtype != torch.bfloat16 or tuple(out.shape) != (M, H):
         raise ValueError("rescale takes fp32 [M, H] in and bf16 [M, H] out")
     _check(lib().shared_mlp_rms_rescale(_ptr(inp), _ptr(out), M, H, _stream(stream, inp.device)))
+
+
+def shared_mlp_linear_plan(M: int, K: int, N: int) -> dict:
+    p = _Plan()
+    _check(lib().shared_mlp_linear_plan(M, K, N, ctypes.byref(p)))
+    d = {k: getattr(p, k) for k, _ in _Plan._fields_}
+    d["path_name"] = PATH_NAMES.get(d["path"], "?")
+    return d
+
+
+def shared_mlp_linear_workspace_bytes(M: int, K: int, N: int) -> int:
+    b = _sz()
+    _check(lib().shared_mlp_linear_workspace_bytes(M, K, N, ctypes.byref(b)))
+    return b.value
+
+
+def shared_mlp_linear(x, w, y, workspace=None, stream=None):
+    """y = x w^T (bf16 x [M, K], w [N, K]; y bf16 or fp32 [M, N]).  y may be a column
+    block of a wider row-major tensor (unit column stride), e.g. a rank's slot of a
+    gathered buffer; its row stride is passed as ldy."""
+    M, K = x.shape
+    N, K2 = w.shape
+    if K2 != K or tuple(y.shape) != (M, N):
+        raise ValueError(f"shapes x {tuple(x.shape)}, w {tuple(w.shape)}, y {tuple(y.shape)} do not match")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or y.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("the projection takes bf16 x and w, and a bf16 or fp32 y")
+    if not y.is_cuda or (N > 1 and y.stride(1) != 1):
+        raise ValueError("y must be a GPU tensor with unit column stride")
+    ldy = y.stride(0) if M > 1 else N
+    need = shared_mlp_linear_workspace_bytes(M, K, N)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().shared_mlp_linear(_ptr(x), _ptr(w), y.data_ptr(), M, K, N, ldy, int(y.dtype == torch.float32),
+                                   _ptr(workspace) if workspace is not None else None,
+                                   workspace.numel() if workspace is not None else 0,
+                                   _stream(stream, x.device)))
+    return y
+
+
+def shared_mlp_restore_logical(gathered, out, sizes, tp: int, stream=None):
+    """Rank-major gathered [M, sum(sizes)] -> logical out (same shape and dtype)."""
+    M, N = gathered.shape
+    if tuple(out.shape) != (M, N) or out.dtype != gathered.dtype:
+        raise ValueError("out must match gathered in shape and dtype")
+    eb = gathered.element_size()
+    arr = (_i64 * max(len(sizes), 1))(*[int(v) for v in sizes])
+    _check(lib().shared_mlp_restore_logical(_ptr(gathered), _ptr(out), M, N, arr, len(sizes), int(tp), eb,
+                                            _stream(stream, gathered.device)))
+    return out

@@ -11,6 +11,7 @@
 
 #include "internal.h"
 #include "smlp.h"
+#include "smlp_latent.h"
 #include "smlp_tuning.h"
 
 namespace {
@@ -62,16 +63,17 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Tuning overrides of the small-M planner (0 = automatic), per stage.
+// Tuning overrides of the small-M planner (0 = automatic), per stage (0 gate_up, 1 down,
+// 2 the plain projection).
 struct SkinnyOverride {
   std::atomic<int> kind{0}, nb{0}, waves{0}, u{0}, ksplit{0};
 };
-SkinnyOverride g_tune[2];
+SkinnyOverride g_tune[3];
 
 struct GemmOverride {
   std::atomic<int> bm{0}, bn{0}, wm{0}, wn{0}, ns{0}, ksplit{0};
 };
-GemmOverride g_gtune[2];
+GemmOverride g_gtune[3];
 
 // Small-M stage plan.  M <= 32: the streaming kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
@@ -114,7 +116,7 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
       for (int c = 0; c < npref; ++c) {
         const int w = o.waves.load() ? o.waves.load() : pref[c][0];
         const int st = o.u.load() ? o.u.load() : pref[c][1];
-        if (smlp::skinny_instantiated(stage == 0, sp.kind, sp.mt, (int)nt, w, st)) {
+        if (smlp::skinny_instantiated(stage, sp.kind, sp.mt, (int)nt, w, st)) {
           sp.waves = w;
           sp.u = st;
           break;
@@ -150,7 +152,7 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     sp.blocks = (int)(groups * ks);
     sp.fpw = 0;
   }
-  if (!smlp::skinny_instantiated(stage == 0, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
+  if (!smlp::skinny_instantiated(stage, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
   *out = sp;
   return true;
 }
@@ -163,9 +165,11 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
 // Two LDS stages, so that two workgroups share a compute unit, and a K split over
 // workgroups when the tiles alone leave compute units idle.  N counts gate_up features
 // (two weight rows each) or down rows.  Returns false if a pinned tile is not compiled.
-bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::GemmPlan* out) {
+// `ov` replaces the stage's tuning overrides (the plain projection plans as down).
+bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::GemmPlan* out,
+               const GemmOverride* ov = nullptr) {
   smlp::GemmPlan gp{};
-  const GemmOverride& o = g_gtune[stage];
+  const GemmOverride& o = ov ? *ov : g_gtune[stage];
   const int64_t fpr = stage == 0 ? 2 : 1;  // weight rows per output feature
   auto tiles_for = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N * fpr + bn - 1) / bn); };
   if (o.bm.load() && o.bn.load()) {
@@ -308,6 +312,96 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
   p->h_offset = 0;
   p->part_offset = p->h_bytes;
   p->workspace_bytes = p->h_bytes + p->part_bytes;
+  return ok();
+}
+
+// Plan of the plain projection y[M, N] = x[M, K] . w[N, K]^T.  M < min(threshold, 33):
+// the streaming kernel, 4 waves with a 4-stage ring, one 16-row tile per workgroup, or
+// two when N has at least 64 tiles (every workgroup re-reads the activations of its K
+// slice, so wider workgroups halve that traffic), and K split over workgroups to about
+// 200 workgroups, with at least 14 K steps per slice.  Measured on MI355X (M = 16,
+// K = 7168): N = 2112 takes 2 tiles x 3 slices (10.9 us), N = 132 one tile x 8 slices
+// (5.9 us), each within noise of the best pinned plan.  Otherwise the LDS-tiled kernel
+// with the down stage's tile rules.
+struct LinearPlan {
+  int path;
+  smlp::SkinnyPlan sk;
+  smlp::GemmPlan gm;
+  int ksplit, blocks;
+  size_t part_bytes;
+};
+
+int make_linear_plan(int64_t M, int64_t K, int64_t N, int64_t ldy, LinearPlan* lp) {
+  if (M < 0) return fail(SMLP_ERR_SHAPE, "M = %lld < 0", (long long)M);
+  if (K < 8 || K % 8 || N < 4 || N % 4)
+    return fail(SMLP_ERR_SHAPE, "projection needs K >= 8, K %% 8 == 0, N >= 4, N %% 4 == 0 (K=%lld N=%lld)",
+                (long long)K, (long long)N);
+  if (ldy < N || ldy % 4)
+    return fail(SMLP_ERR_SHAPE, "ldy = %lld must be >= N = %lld and a multiple of 4", (long long)ldy,
+                (long long)N);
+  if (K >= kLimit || N >= kLimit || ldy >= kLimit || M * K >= kLimit || N * K >= kLimit ||
+      M * ldy >= kLimit)
+    return fail(SMLP_ERR_SHAPE, "sizes too large: M*K, N*K and M*ldy must be < 2^31");
+  std::memset(lp, 0, sizeof *lp);
+  if (M == 0) {
+    lp->path = SMLP_PATH_NONE;
+    return ok();
+  }
+  const int64_t thr = g_threshold.load() < 33 ? g_threshold.load() : 33;
+  if (M < thr) {
+    using namespace smlp;
+    const SkinnyOverride& o = g_tune[2];
+    SkinnyPlan& sp = lp->sk;
+    if (o.kind.load() && o.kind.load() != SKINNY_STREAM16)
+      return fail(SMLP_ERR_ARG, "the projection's small-M kernel is kind %d only", SKINNY_STREAM16);
+    sp.kind = SKINNY_STREAM16;
+    sp.mt = M <= 16 ? 1 : 2;
+    const int64_t tiles16 = (N + 15) / 16;
+    int64_t nt = o.nb.load() ? o.nb.load() : (tiles16 >= 64 ? 2 : 1);
+    if (nt > 4) nt = 4;
+    sp.nb = (int)nt;
+    sp.fpw = (int)(16 * nt);
+    const int64_t groups = (N + sp.fpw - 1) / sp.fpw;
+    static const int kPref[][2] = {{4, 4}, {8, 3}, {4, 6}, {8, 2}};
+    sp.waves = o.waves.load();
+    sp.u = o.u.load();
+    if (!sp.waves || !sp.u) {
+      for (const auto& c : kPref) {
+        const int w = sp.waves ? sp.waves : c[0], st = sp.u ? sp.u : c[1];
+        if (skinny_instantiated(2, sp.kind, sp.mt, sp.nb, w, st)) {
+          sp.waves = w;
+          sp.u = st;
+          break;
+        }
+      }
+    }
+    if (!sp.waves || !sp.u || !skinny_instantiated(2, sp.kind, sp.mt, sp.nb, sp.waves, sp.u))
+      return fail(SMLP_ERR_ARG, "the pinned projection tuning is not a compiled configuration");
+    const int64_t ksteps = (K + 63) / 64;
+    int64_t ks = o.ksplit.load();
+    if (!ks) {
+      ks = (200 + groups / 2) / groups;
+      const int64_t max_ks = ksteps / 14;
+      if (ks > max_ks) ks = max_ks;
+      if (ks < 1) ks = 1;
+    }
+    if (ks > ksteps) ks = ksteps;
+    const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
+    ks = (K + kslice - 1) / kslice;
+    sp.ksplit = (int)ks;
+    sp.kslice = (int)kslice;
+    sp.blocks = (int)(groups * ks);
+    lp->path = SMLP_PATH_SMALL_M;
+    lp->ksplit = sp.ksplit;
+    lp->blocks = sp.blocks;
+  } else {
+    if (!plan_gemm(1, M, N, K, false, &lp->gm, &g_gtune[2]))
+      return fail(SMLP_ERR_ARG, "the pinned projection tile is not a compiled configuration");
+    lp->path = SMLP_PATH_LARGE_M;
+    lp->ksplit = lp->gm.ksplit;
+    lp->blocks = lp->gm.tiles * lp->gm.ksplit;
+  }
+  lp->part_bytes = lp->ksplit > 1 ? round_up((size_t)lp->ksplit * M * N * 4, 256) : 0;
   return ok();
 }
 
@@ -466,6 +560,95 @@ int shared_mlp_down(const void* w_down, void* out, int64_t M, int64_t H, int64_t
              workspace_bytes, stream);
 }
 
+int shared_mlp_linear_plan(int64_t M, int64_t K, int64_t N, smlp_plan* plan) {
+  if (!plan) return fail(SMLP_ERR_NULL, "plan is NULL");
+  LinearPlan lp;
+  int rc = make_linear_plan(M, K, N, N, &lp);
+  if (rc) return rc;
+  std::memset(plan, 0, sizeof *plan);
+  plan->path = lp.path;
+  plan->h_dtype = SMLP_BF16;
+  plan->workspace_bytes = lp.part_bytes;
+  plan->down_ksplit = lp.path == SMLP_PATH_NONE ? 1 : lp.ksplit;
+  plan->down_blocks = lp.blocks;
+  plan->kernels = lp.path == SMLP_PATH_NONE ? 0 : 1 + (lp.ksplit > 1);
+  return ok();
+}
+
+int shared_mlp_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
+  if (!bytes) return fail(SMLP_ERR_NULL, "bytes is NULL");
+  LinearPlan lp;
+  int rc = make_linear_plan(M, K, N, N, &lp);
+  if (rc) return rc;
+  *bytes = lp.part_bytes;
+  return ok();
+}
+
+int shared_mlp_linear(const void* x, const void* w, void* y, int64_t M, int64_t K, int64_t N,
+                      int64_t ldy, int out_fp32, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (out_fp32 != 0 && out_fp32 != 1) return fail(SMLP_ERR_DTYPE, "out_fp32 = %d is neither 0 nor 1", out_fp32);
+  LinearPlan lp;
+  int rc = make_linear_plan(M, K, N, ldy, &lp);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  const size_t oe = out_fp32 ? 4 : 2;
+  if ((rc = check_ptr(x, "x", 16)) || (rc = check_ptr(w, "w", 16)) || (rc = check_ptr(y, "y", 4 * oe)))
+    return rc;
+  if (lp.part_bytes) {
+    if ((rc = check_ptr(workspace, "workspace", 256))) return rc;
+    if (workspace_bytes < lp.part_bytes)
+      return fail(SMLP_ERR_WORKSPACE, "workspace_bytes = %zu < %zu needed", workspace_bytes, lp.part_bytes);
+  }
+  const size_t x_n = (size_t)(M * K) * 2, w_n = (size_t)(N * K) * 2,
+               y_n = ((size_t)(M - 1) * ldy + N) * oe;
+  if (overlap(y, y_n, x, x_n) || overlap(y, y_n, w, w_n) || overlap(y, y_n, workspace, lp.part_bytes))
+    return fail(SMLP_ERR_ALIAS, "y overlaps x, w or the workspace");
+  if (overlap(workspace, lp.part_bytes, x, x_n) || overlap(workspace, lp.part_bytes, w, w_n))
+    return fail(SMLP_ERR_ALIAS, "workspace overlaps x or w");
+  (void)hipGetLastError();
+  float* part = static_cast<float*>(workspace);
+  if (lp.path == SMLP_PATH_SMALL_M)
+    rc = smlp::launch_skinny_linear(lp.sk, x, w, y, (int)M, (int)K, (int)N, (int)ldy, out_fp32, part, stream);
+  else
+    rc = smlp::launch_gemm_linear(lp.gm, x, w, y, (int)M, (int)K, (int)N, (int)ldy, out_fp32, part, stream);
+  if ((rc = hip_status(rc, "projection launch"))) return rc;
+  return ok();
+}
+
+int shared_mlp_restore_logical(const void* gathered, void* out, int64_t M, int64_t n_gathered,
+                               const int64_t* sizes, int nsizes, int tp, int elem_bytes,
+                               hipStream_t stream) {
+  if (!sizes) return fail(SMLP_ERR_NULL, "sizes is NULL");
+  if (nsizes < 1 || nsizes > SMLP_MAX_RANGES)
+    return fail(SMLP_ERR_ARG, "nsizes = %d outside [1, %d]", nsizes, SMLP_MAX_RANGES);
+  if (elem_bytes != 2 && elem_bytes != 4)
+    return fail(SMLP_ERR_ARG, "elem_bytes = %d is neither 2 nor 4", elem_bytes);
+  if (tp < 1) return fail(SMLP_ERR_SHAPE, "tp = %d < 1", tp);
+  int64_t total = 0;
+  for (int t = 0; t < nsizes; ++t) {
+    if (sizes[t] <= 0 || sizes[t] % tp)
+      return fail(SMLP_ERR_SHAPE, "range %d has size %lld, not a positive multiple of tp = %d", t,
+                  (long long)sizes[t], tp);
+    if (sizes[t] >= kLimit) return fail(SMLP_ERR_SHAPE, "range %d is too large", t);
+    total += sizes[t];
+  }
+  if (n_gathered != total)
+    return fail(SMLP_ERR_SHAPE, "gathered width %lld does not match the ranges (sum %lld)",
+                (long long)n_gathered, (long long)total);
+  if (M < 0 || M * n_gathered >= kLimit)
+    return fail(SMLP_ERR_SHAPE, "M = %lld out of range (M * n_gathered < 2^31)", (long long)M);
+  if (M == 0) return ok();
+  int rc;
+  if ((rc = check_ptr(gathered, "gathered", elem_bytes)) || (rc = check_ptr(out, "out", elem_bytes))) return rc;
+  const size_t n = (size_t)(M * n_gathered) * elem_bytes;
+  if (overlap(gathered, n, out, n)) return fail(SMLP_ERR_ALIAS, "out overlaps gathered");
+  (void)hipGetLastError();
+  rc = smlp::launch_restore_logical(gathered, out, M, n_gathered, sizes, nsizes, tp, elem_bytes, stream);
+  if ((rc = hip_status(rc, "restore launch"))) return rc;
+  return ok();
+}
+
 int64_t shared_mlp_set_large_m_threshold(int64_t threshold) {
   if (threshold < 1 || threshold > kSmallMaxM + 1) {
     fail(SMLP_ERR_ARG, "threshold %lld outside [1, %lld]", (long long)threshold,
@@ -477,8 +660,9 @@ int64_t shared_mlp_set_large_m_threshold(int64_t threshold) {
 }
 
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit) {
-  if (stage < 0 || stage > 1 || kind < 0 || kind == 1 || kind > 3 || !(nb == 0 || nb == 1 || nb == 2 || nb == 4) ||
-      !(waves == 0 || waves == 4 || waves == 8) || u < 0 || u > 5 || ksplit < 0 || ksplit > 1024)
+  if (stage < 0 || stage > 2 || kind < 0 || kind == 1 || kind > 3 || (stage == 2 && kind == 2) ||
+      !(nb == 0 || nb == 1 || nb == 2 || nb == 3 || nb == 4) ||
+      !(waves == 0 || waves == 4 || waves == 8) || u < 0 || u > 8 || ksplit < 0 || ksplit > 1024)
     return fail(SMLP_ERR_ARG, "bad small-M tuning (stage %d kind %d nb %d waves %d u %d ksplit %d)",
                 stage, kind, nb, waves, u, ksplit);
   g_tune[stage].kind = kind;
@@ -490,7 +674,7 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
 }
 
 int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit) {
-  if (stage < 0 || stage > 1 || !(bm == 0 || bm == 128 || bm == 256) ||
+  if (stage < 0 || stage > 2 || !(bm == 0 || bm == 128 || bm == 256) ||
       !(bn == 0 || bn == 32 || bn == 64 || bn == 128 || bn == 256) || (bm == 0) != (bn == 0) ||
       !(wm == 0 || wm == 1 || wm == 2 || wm == 4) || !(wn == 0 || wn == 1 || wn == 2 || wn == 4) ||
       (wm == 0) != (wn == 0) || ns < 0 || ns > 8 || ksplit < 0 || ksplit > 1024)

@@ -49,6 +49,7 @@ struct GArgs {
   int tiles_m, tiles_n;
   int kslice;             // K elements per workgroup slice (gridDim.y slices)
   void* out;              // gate_up: h plane(s); down: out [M, N] bf16 or fp32
+  int ldo;                // down: elements between output rows (>= N)
   float* part;            // gridDim.y > 1: fp32 partial sums [slices][M][P*N]
   int out_f32;
   int h_planes;           // gate_up: planes of h to store (1 or 2)
@@ -293,9 +294,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
           if (split)
             g.part[((size_t)slice * g.M + m) * (size_t)g.N + n] = v;
           else if (g.out_f32)
-            reinterpret_cast<float*>(g.out)[(size_t)m * g.N + n] = v;
+            reinterpret_cast<float*>(g.out)[(size_t)m * g.ldo + n] = v;
           else
-            reinterpret_cast<uint16_t*>(g.out)[(size_t)m * g.N + n] = (uint16_t)f2bf(v);
+            reinterpret_cast<uint16_t*>(g.out)[(size_t)m * g.ldo + n] = (uint16_t)f2bf(v);
         }
       }
     }
@@ -362,12 +363,13 @@ int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, voi
   a.tiles_n = p.ggu.tiles / p.ggu.tiles_m;
   a.kslice = p.ggu.kslice;
   a.out = static_cast<char*>(ws) + p.h_offset;
+  a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = 0;
   a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
   int rc = launch_mode<GM_GATE_UP>(p.ggu, a, s);
   if (rc || p.ggu.ksplit == 1) return rc;
-  return launch_finalize(true, a.part, p.ggu.ksplit, a.M, a.N, a.out, 0, a.h_planes, s);
+  return launch_finalize(true, a.part, p.ggu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);
 }
 
 int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
@@ -385,13 +387,39 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
   a.tiles_n = p.gdn.tiles / p.gdn.tiles_m;
   a.kslice = p.gdn.kslice;
   a.out = out;
+  a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = p.partial_fp32 ? 1 : 0;
   a.h_planes = 1;
   int rc = p.h_dtype == SMLP_BF16_HILO ? launch_mode<GM_DOWN_HILO>(p.gdn, a, s)
                                       : launch_mode<GM_DOWN_BF16>(p.gdn, a, s);
   if (rc || p.gdn.ksplit == 1) return rc;
-  return launch_finalize(false, a.part, p.gdn.ksplit, a.M, a.N, out, a.out_f32, 1, s);
+  return launch_finalize(false, a.part, p.gdn.ksplit, a.M, a.N, out, a.N, a.out_f32, 1, s);
+}
+
+// A plain projection y = x . w^T runs the down stage's one-plane kernel with A = x.
+int launch_gemm_linear(const GemmPlan& gp, const void* x, const void* w, void* y, int M, int K,
+                       int N, int ldy, int out_f32, float* part, hipStream_t s) {
+  GArgs a{};
+  a.a = reinterpret_cast<const uint16_t*>(x);
+  a.a_lo = nullptr;
+  a.b = reinterpret_cast<const uint16_t*>(w);
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.up_off = 0;
+  a.b_rows = N;
+  a.tiles_m = gp.tiles_m;
+  a.tiles_n = gp.tiles / gp.tiles_m;
+  a.kslice = gp.kslice;
+  a.out = y;
+  a.ldo = ldy;
+  a.part = part;
+  a.out_f32 = out_f32;
+  a.h_planes = 1;
+  int rc = launch_mode<GM_DOWN_BF16>(gp, a, s);
+  if (rc || gp.ksplit == 1) return rc;
+  return launch_finalize(false, part, gp.ksplit, M, N, y, ldy, out_f32, 1, s);
 }
 
 }  // namespace smlp

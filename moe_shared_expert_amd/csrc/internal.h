@@ -50,7 +50,7 @@ struct Plan {
 };
 
 // Weight-streaming stages (skinny.hip).  Return a hipError_t.
-bool skinny_instantiated(bool gate_up, int kind, int mt, int nb, int waves, int u);
+bool skinny_instantiated(int stage, int kind, int mt, int nb, int waves, int u);  // stage 0 gate_up, 1 down, 2 projection
 int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
                           hipStream_t s);
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
@@ -58,7 +58,19 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
 // Sum K-split partials [ksplit][M][P*N] in slice order and apply the stage epilogue
 // (gate_up: SiLU-and-mul into h with `h_planes` bf16 planes; down: bf16 or fp32 out).
 int launch_finalize(bool gate_up, const float* part, int ksplit, int M, int N, void* out,
-                    int out_f32, int h_planes, hipStream_t s);
+                    int ldo, int out_f32, int h_planes, hipStream_t s);
+
+// Plain projection y = x . w^T (bf16 operands; y bf16 or fp32 with row stride ldy):
+// the streaming kernel (plan kind SKINNY_STREAM16, M <= 32) or the LDS-tiled kernel,
+// with `part` holding ksplit x M x N fp32 partials when the plan splits K.
+int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, void* y, int M, int K,
+                         int N, int ldy, int out_f32, float* part, hipStream_t s);
+int launch_gemm_linear(const GemmPlan& gp, const void* x, const void* w, void* y, int M, int K,
+                       int N, int ldy, int out_f32, float* part, hipStream_t s);
+// Rank-major -> logical column order of a gathered merged-column output (latent.hip);
+// arguments validated by the caller.
+int launch_restore_logical(const void* src, void* dst, int64_t M, int64_t N, const int64_t* sizes,
+                           int nr, int tp, int elem_bytes, hipStream_t s);
 
 // LDS-tiled GEMM stages (gemm.hip).
 bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns);  // stage 0: gate_up, 1: down

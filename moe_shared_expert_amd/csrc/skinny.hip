@@ -1,5 +1,6 @@
 // Weight-streaming kernels for small token counts (decode): the gate_up projection
-// with the SiLU-and-mul epilogue, and the down projection.
+// with the SiLU-and-mul epilogue, the down projection, and a plain projection y = x.w^T
+// (the merged MLA latent projection, streaming kind only).
 //
 // Shape of the work: C[M, N] = A[M, K] . W[N, K]^T with M small (<= 128) and W large.
 // Every weight byte is used by all M tokens and by nothing else, so the kernels are
@@ -31,8 +32,9 @@
 
 namespace smlp {
 
-// Kernel modes: the gate_up stage, and the down stage reading h as two bf16 planes.
-enum { MODE_GATE_UP = 0, MODE_DOWN_HILO = 1 };
+// Kernel modes: the gate_up stage, the down stage reading h as two bf16 planes, and a
+// plain projection (one bf16 activation plane, no epilogue; streaming kind only).
+enum { MODE_GATE_UP = 0, MODE_DOWN_HILO = 1, MODE_LINEAR = 2 };
 
 struct SkArgs {
   const uint16_t* a_hi;  // [M, K] bf16 activations (x), or the hi plane of h
@@ -42,6 +44,7 @@ struct SkArgs {
   int up_off;            // gate_up: first row of the up projection (= I)
   int kslice;            // K elements per workgroup (multiple of 64)
   void* out;             // ksplit == 1: gate_up -> h planes, down -> out [M, N]
+  int ldo;               // down / projection: elements between output rows (>= N)
   float* part;           // ksplit > 1: partial sums [ksplit][M][P*N]
   int out_f32;           // down: fp32 (1) or bf16 (0) output
   int h_planes;          // gate_up (and its finalize): h planes to store, 2 on this path
@@ -123,9 +126,9 @@ __device__ __forceinline__ void finish_workgroup(const SkArgs& a,
         } else if (GU) {
           store_h(a.out, a.M, a.N, m, n, silu_mul(acc[0][nb][mt][j], acc[P - 1][nb][mt][j]), a.h_planes);
         } else if (a.out_f32) {
-          reinterpret_cast<float*>(a.out)[(size_t)m * a.N + n] = acc[0][nb][mt][j];
+          reinterpret_cast<float*>(a.out)[(size_t)m * a.ldo + n] = acc[0][nb][mt][j];
         } else {
-          reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.N + n] = (uint16_t)f2bf(acc[0][nb][mt][j]);
+          reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] = (uint16_t)f2bf(acc[0][nb][mt][j]);
         }
       }
     }
@@ -147,7 +150,7 @@ __device__ __forceinline__ void finish_workgroup(const SkArgs& a,
 template <int MT, int NT, int WAVES, int STAGES, int MODE>
 __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   constexpr bool GU = MODE == MODE_GATE_UP;
-  constexpr int NA = GU ? 1 : 2;        // activation planes: x, or h hi + lo
+  constexpr int NA = MODE == MODE_DOWN_HILO ? 2 : 1;  // activation planes: x, or h hi + lo
   constexpr int TA = NA * MT;           // activation tiles per K step
   constexpr int TT = NT + TA;           // 2 KB tiles per K step
   constexpr int SLOT = TT * 2048;       // one ring slot: one K step of this wave
@@ -166,7 +169,19 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   const int K = a.K;
   char* my = lds + wave * WAVE_LDS;
 
-  const int f0 = blockIdx.x * a.fpw;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  With
+  // a K split, the (slice, column) order is cut into one contiguous run per XCD, so an
+  // XCD holds whole K slices and fetches only its slices of the activations.
+  int col = blockIdx.x, slice = blockIdx.y;
+  if (gridDim.y > 1) {
+    const int total = gridDim.x * gridDim.y;
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = lin % 8, per = total / 8, rem = total % 8;
+    const int t = xcd * per + min(xcd, rem) + lin / 8;
+    slice = t / gridDim.x;
+    col = t % gridDim.x;
+  }
+  const int f0 = col * a.fpw;
   const int fend = min(a.N, f0 + a.fpw);
   const uint32_t wbytes = (uint32_t)a.w_rows * (uint32_t)K * 2u;
   const uint32_t abytes = (uint32_t)a.M * (uint32_t)K * 2u;
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kbeg = blockIdx.y * a.kslice;
+  const int kbeg = slice * a.kslice;
   const int kend = min(K, kbeg + a.kslice);
   constexpr int STEP = 64 * WAVES;
   const int nst = (kend - kbeg + STEP - 1) / STEP;
@@ -313,7 +328,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
           if (m >= a.M || f >= fend) continue;
           if (ksplit > 1) {
             // lanes 0-7 hold gate columns, lanes 8-15 the matching up columns
-            a.part[((size_t)blockIdx.y * a.M + m) * (size_t)(2 * a.N) + (ln < 8 ? f : a.N + f)] = v;
+            a.part[((size_t)slice * a.M + m) * (size_t)(2 * a.N) + (ln < 8 ? f : a.N + f)] = v;
           } else if (ln < 8) {
             store_h(a.out, a.M, a.N, m, f, silu_mul(v, up), a.h_planes);
           }
@@ -321,11 +336,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
           const int n = f0 + 16 * t + ln;
           if (m >= a.M || n >= fend) continue;
           if (ksplit > 1)
-            a.part[((size_t)blockIdx.y * a.M + m) * (size_t)a.N + n] = v;
+            a.part[((size_t)slice * a.M + m) * (size_t)a.N + n] = v;
           else if (a.out_f32)
-            reinterpret_cast<float*>(a.out)[(size_t)m * a.N + n] = v;
+            reinterpret_cast<float*>(a.out)[(size_t)m * a.ldo + n] = v;
           else
-            reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.N + n] = (uint16_t)f2bf(v);
+            reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] = (uint16_t)f2bf(v);
         }
       }
 }
@@ -476,9 +491,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_direct_kernel(SkArgs a) {
 template <bool GU>
 __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__ part,
                                                        int ksplit, int M, int N, void* out,
-                                                       int out_f32, int h_planes) {
+                                                       int ldo, int out_f32, int h_planes) {
   // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, four
-  // slices in flight at a time, summed in slice order.
+  // slices in flight at a time, summed in slice order.  Down and projection outputs
+  // have row stride ldo (a multiple of 4).
   constexpr int P = GU ? 2 : 1;
   const int N4 = N >> 2;
   const size_t total = (size_t)M * N4;
@@ -506,7 +522,7 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
       g += *reinterpret_cast<const f32x4*>(base + (size_t)s * sstride);
       if (GU) u += *reinterpret_cast<const f32x4*>(base + (size_t)s * sstride + N);
     }
-    const size_t o = (size_t)m * N + n;
+    const size_t o = (size_t)m * (GU ? N : ldo) + n;
     if (GU) {
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -540,12 +556,20 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
 #define SMLP_SK_DN_STREAM16(X)                                                                 \
   X(1, 1, 4, 4) X(1, 1, 8, 3) X(1, 2, 4, 3) X(1, 2, 4, 4) X(1, 2, 4, 5) X(1, 2, 8, 2)          \
   X(1, 3, 4, 4) X(1, 4, 4, 3) X(2, 1, 4, 4) X(2, 2, 4, 3) X(2, 3, 4, 2) X(2, 4, 4, 2)
+// Projection (one activation plane): deeper rings, so that a wave keeps more weight
+// bytes in flight when a workgroup holds only one or two 16-row tiles.
+#define SMLP_SK_LIN_STREAM16(X)                                                                \
+  X(1, 1, 4, 4) X(1, 1, 4, 6) X(1, 1, 4, 8) X(1, 1, 8, 3) X(1, 1, 8, 4) X(1, 1, 8, 5)          \
+  X(1, 2, 4, 4) X(1, 2, 4, 6) X(1, 2, 8, 3) X(1, 3, 4, 4) X(1, 4, 4, 4) X(2, 1, 4, 4)          \
+  X(2, 1, 4, 6) X(2, 1, 8, 3) X(2, 2, 4, 4) X(2, 2, 8, 2)
 #define SMLP_SK_GU_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1) X(8, 1, 8, 1)
 #define SMLP_SK_DN_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1)
-bool skinny_instantiated(bool gu, int kind, int mt, int nb, int waves, int u) {
+bool skinny_instantiated(int stage, int kind, int mt, int nb, int waves, int u) {
 #define SMLP_MATCH(MT_, NB_, W_, U_) \
   if (mt == MT_ && nb == NB_ && waves == W_ && u == U_) return true;
-  if (gu) {
+  if (stage == 2) {
+    if (kind == SKINNY_STREAM16) { SMLP_SK_LIN_STREAM16(SMLP_MATCH) }
+  } else if (stage == 0) {
     if (kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_MATCH) }
     if (kind == SKINNY_STREAM16) { SMLP_SK_GU_STREAM16(SMLP_MATCH) }
   } else {
@@ -575,6 +599,8 @@ static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
   if constexpr (GU) {
     if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_SK_D) }
     if (sp.kind == SKINNY_STREAM16) { SMLP_SK_GU_STREAM16(SMLP_SK_S) }
+  } else if constexpr (MODE == MODE_LINEAR) {
+    if (sp.kind == SKINNY_STREAM16) { SMLP_SK_LIN_STREAM16(SMLP_SK_S) }
   } else {
     if (sp.kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_SK_D) }
     if (sp.kind == SKINNY_STREAM16) { SMLP_SK_DN_STREAM16(SMLP_SK_S) }
@@ -585,18 +611,18 @@ static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
   return (int)hipErrorInvalidConfiguration;
 }
 
-int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int out_f32,
-                    int h_planes, hipStream_t s) {
-  if (N % 4 != 0) return (int)hipErrorInvalidValue;  // bf16 shapes have N % 8 == 0
+int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int ldo,
+                    int out_f32, int h_planes, hipStream_t s) {
+  if (N % 4 != 0 || ldo % 4 != 0) return (int)hipErrorInvalidValue;
   const size_t total = (size_t)M * (N / 4);
   int blocks = (int)((total + 255) / 256);
   if (blocks > 2048) blocks = 2048;
   if (gu)
     hipLaunchKernelGGL(skinny_finalize<true>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
-                       out, out_f32, h_planes);
+                       out, ldo, out_f32, h_planes);
   else
     hipLaunchKernelGGL(skinny_finalize<false>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
-                       out, out_f32, h_planes);
+                       out, ldo, out_f32, h_planes);
   return (int)hipGetLastError();
 }
 
@@ -612,6 +638,7 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.up_off = (int)p.I;
   a.kslice = p.gu.kslice;
   a.out = static_cast<char*>(ws) + p.h_offset;
+  a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = 0;
   a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
@@ -619,7 +646,7 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.w_rows = (int)(2 * p.I);
   int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
   if (rc || p.gu.ksplit == 1) return rc;
-  return launch_finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, 0, a.h_planes, s);
+  return launch_finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);
 }
 
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
@@ -634,6 +661,7 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.up_off = 0;
   a.kslice = p.dn.kslice;
   a.out = out;
+  a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = p.partial_fp32 ? 1 : 0;
   a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
@@ -641,7 +669,30 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.w_rows = (int)p.H;
   int rc = launch_stage<MODE_DOWN_HILO>(p.dn, a, s);
   if (rc || p.dn.ksplit == 1) return rc;
-  return launch_finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.out_f32, 1, s);
+  return launch_finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.N, a.out_f32, 1, s);
+}
+
+int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, void* y, int M, int K,
+                         int N, int ldy, int out_f32, float* part, hipStream_t s) {
+  SkArgs a;
+  a.a_hi = reinterpret_cast<const uint16_t*>(x);
+  a.a_lo = nullptr;
+  a.w = reinterpret_cast<const uint16_t*>(w);
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.up_off = 0;
+  a.kslice = sp.kslice;
+  a.out = y;
+  a.ldo = ldy;
+  a.part = part;
+  a.out_f32 = out_f32;
+  a.h_planes = 1;
+  a.fpw = sp.fpw;
+  a.w_rows = N;
+  int rc = launch_stage<MODE_LINEAR>(sp, a, s);
+  if (rc || sp.ksplit == 1) return rc;
+  return launch_finalize(false, part, sp.ksplit, M, N, y, ldy, out_f32, 1, s);
 }
 
 }  // namespace smlp

@@ -31,3 +31,16 @@ def algorithmic_bytes(m: int, hidden: int, inter: int, in_elem: int = 2,
 
 def flops(m: int, hidden: int, inter: int) -> int:
     return 6 * m * hidden * inter
+
+
+# Merged MLA latent projection (vLLM PR 345): y_r = x . W_r^T for one rank's column
+# shard W_r [n_r, K], then the restore of the gathered [M, n] output to logical order.
+
+def latent_projection_bytes(m: int, k: int, n_r: int, elem: int = 2, out_elem: int = 2) -> int:
+    """Weight shard once, x once, the rank's output slot once."""
+    return n_r * k * elem + m * k * elem + m * n_r * out_elem
+
+
+def latent_restore_bytes(m: int, n: int, elem: int = 2) -> int:
+    """The gathered output read once and the logical output written once."""
+    return 2 * m * n * elem

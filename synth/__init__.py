@@ -23,6 +23,11 @@ Recipes
   with round-to-nearest-even (torch's conversion).
 * Seeds: ``1000 * config + 10 * copy + tensor_id`` with tensor_id x=0, gate=1,
   up=2, down=3; the per-layer stack uses copy = layer index.
+* Merged MLA latent projection (vLLM PR 345, "[II] TP-shard Kimi MLA latent
+  projections", section "Behavior": 24 layers of 2112 x 7168 bf16): the q_a range
+  followed by the kv_a range, taken as 1536 + 576 rows (the page gives only the
+  total); x ~ N(0, 1), w ~ N(0, 1/7168); config 6, tensor_id 4 for the weight, so
+  ``seed_of(6, layer, 4)``.
 """
 from __future__ import annotations
 
@@ -32,7 +37,11 @@ import torch
 HIDDEN = 7168          # Kimi-K3 hidden size
 INTERMEDIATE = 6144    # Kimi-K3 shared-expert intermediate size
 
-TID_X, TID_GATE, TID_UP, TID_DOWN = 0, 1, 2, 3
+TID_X, TID_GATE, TID_UP, TID_DOWN, TID_LATENT = 0, 1, 2, 3, 4
+
+LATENT_SIZES = (1536, 576)   # q_a rows, kv_a rows of the merged latent projection
+LATENT_LAYERS = 24           # MLA layers of Kimi-K3
+LATENT_CONFIG = 6
 
 
 def seed_of(config: int, copy: int, tensor_id: int) -> int:
@@ -91,6 +100,12 @@ def layer_weights(hidden: int, intermediate: int, config: int, copy: int = 0,
     up = normal((intermediate, hidden), sg, seed_of(config, copy, TID_UP), dtype)
     down = normal((hidden, intermediate), sd, seed_of(config, copy, TID_DOWN), dtype)
     return merged_gate_up(gate, up), down
+
+
+def latent_weight(rows: int, hidden: int, copy: int = 0, config: int = LATENT_CONFIG,
+                  dtype=torch.bfloat16) -> torch.Tensor:
+    """One layer's merged latent projection weight [rows, hidden] ~ N(0, 1/hidden)."""
+    return normal((rows, hidden), float(hidden) ** -0.5, seed_of(config, copy, TID_LATENT), dtype)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

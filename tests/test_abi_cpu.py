@@ -33,8 +33,8 @@ def _declared(header):
 
 
 def test_every_declared_symbol_is_exported(L):
-    names = _declared("smlp.h")
-    assert len(names) >= 11
+    names = _declared("smlp.h") + _declared("smlp_latent.h")
+    assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTS), "binding and header disagree"
@@ -60,13 +60,15 @@ def test_tuning_hook(L):
         with pytest.raises(binding.SmlpError):
             binding.shared_mlp_plan(64, H, I)   # the streaming kind serves M <= 32 only
         with pytest.raises(binding.SmlpError):
-            binding.shared_mlp_tune_skinny(0, nb=3)
+            binding.shared_mlp_tune_skinny(0, nb=5)
         with pytest.raises(binding.SmlpError):
             binding.shared_mlp_tune_skinny(0, kind=4)
         with pytest.raises(binding.SmlpError):
             binding.shared_mlp_tune_skinny(0, kind=1)   # retired kind
         with pytest.raises(binding.SmlpError):
-            binding.shared_mlp_tune_skinny(2)
+            binding.shared_mlp_tune_skinny(3)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_skinny(2, kind=2)   # the projection streams only
     finally:
         binding.shared_mlp_tune_skinny(0)
         binding.shared_mlp_set_large_m_threshold(prev)
@@ -92,7 +94,7 @@ def test_default_threshold_and_gemm_tuning(L):
             with pytest.raises(binding.SmlpError):
                 binding.shared_mlp_tune_gemm(0, **bad)
         with pytest.raises(binding.SmlpError):
-            binding.shared_mlp_tune_gemm(2)
+            binding.shared_mlp_tune_gemm(3)
     finally:
         binding.shared_mlp_tune_gemm(0)
 
