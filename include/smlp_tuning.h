@@ -31,6 +31,13 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
  * makes later plans fail with SMLP_ERR_ARG. */
 int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit);
 
+/* Planes of the intermediate h on the small-M (weight-streaming) path: 1 = one bf16
+ * plane (h rounded once to bf16, as the serving stack stores it; the down stage then
+ * runs the projection kernel, M <= 32 only), 2 = two planes hi + lo (h effectively
+ * unrounded), 0 = automatic (one plane for M <= 32 and I >= 256, else two).
+ * Process-wide, for subsequent plans.  Returns SMLP_OK or SMLP_ERR_ARG. */
+int shared_mlp_tune_h_planes(int planes);
+
 #ifdef __cplusplus
 }
 #endif

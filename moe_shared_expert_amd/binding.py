@@ -65,6 +65,7 @@ EXPORTS = {
 TUNING_EXPORTS = {
     "shared_mlp_tune_skinny": (_int, [_int, _int, _int, _int, _int, _int]),
     "shared_mlp_tune_gemm": (_int, [_int, _int, _int, _int, _int, _int, _int]),
+    "shared_mlp_tune_h_planes": (_int, [_int]),
 }
 
 
@@ -198,6 +199,11 @@ def shared_mlp_tune_gemm(stage: int, bm: int = 0, bn: int = 0, wm: int = 0, wn: 
                          ksplit: int = 0):
     """Pin large-M tile parameters (0 = automatic); see include/smlp_tuning.h."""
     _check(lib().shared_mlp_tune_gemm(stage, bm, bn, wm, wn, ns, ksplit))
+
+
+def shared_mlp_tune_h_planes(planes: int = 0):
+    """Planes of h on the small-M path (0 = automatic); see include/smlp_tuning.h."""
+    _check(lib().shared_mlp_tune_h_planes(planes))
 
 
 def forward(x, w_gate_up, w_down, partial_fp32=False, workspace=None, stream=None):

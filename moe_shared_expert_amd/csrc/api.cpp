@@ -75,14 +75,20 @@ struct GemmOverride {
 };
 GemmOverride g_gtune[3];
 
+// Planes of h on the small-M path (0 = automatic: two), see shared_mlp_tune_h_planes.
+std::atomic<int> g_h_planes{0};
+
 // Small-M stage plan.  M <= 32: the streaming kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
 // range, waves interleaved over K.  M > 32: the direct-load kernel over 16-feature
 // blocks, with a K split over workgroups when the blocks alone cannot keep about
 // three waves per compute unit streaming.  Returns false if a pinned (tuned)
 // configuration is not one of the compiled kernels.
-bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* out) {
+// `inst` names the compiled config list the plan must come from (default: the stage's
+// own; the down stage with one plane of h runs the projection kernel, list 2).
+bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* out, int inst = -1) {
   using namespace smlp;
+  if (inst < 0) inst = stage;
   const SkinnyOverride& o = g_tune[stage];
   smlp::SkinnyPlan sp{};
   sp.kind = o.kind.load() ? o.kind.load() : (M <= 32 ? SKINNY_STREAM16 : SKINNY_DIRECT16);
@@ -110,13 +116,14 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     // this order.
     static const int kPrefGU[][2] = {{4, 3}, {4, 4}, {4, 2}, {8, 2}};
     static const int kPrefDN[][2] = {{8, 2}, {8, 3}, {4, 4}, {4, 3}, {4, 2}};
-    const int (*pref)[2] = stage == 0 ? kPrefGU : kPrefDN;
-    const int npref = stage == 0 ? 4 : 5;
+    static const int kPrefDN1[][2] = {{8, 3}, {4, 4}, {8, 2}, {4, 6}};
+    const int (*pref)[2] = stage == 0 ? kPrefGU : inst == 2 ? kPrefDN1 : kPrefDN;
+    const int npref = stage == 0 ? 4 : inst == 2 ? 4 : 5;
     if (!o.waves.load() || !o.u.load()) {
       for (int c = 0; c < npref; ++c) {
         const int w = o.waves.load() ? o.waves.load() : pref[c][0];
         const int st = o.u.load() ? o.u.load() : pref[c][1];
-        if (smlp::skinny_instantiated(stage, sp.kind, sp.mt, (int)nt, w, st)) {
+        if (smlp::skinny_instantiated(inst, sp.kind, sp.mt, (int)nt, w, st)) {
           sp.waves = w;
           sp.u = st;
           break;
@@ -152,7 +159,7 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     sp.blocks = (int)(groups * ks);
     sp.fpw = 0;
   }
-  if (!smlp::skinny_instantiated(stage, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
+  if (!smlp::skinny_instantiated(inst, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
   *out = sp;
   return true;
 }
@@ -275,11 +282,18 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     p->kernels = 2;
   } else if (M < g_threshold.load() && M <= kSmallMaxM) {
     p->path = SMLP_PATH_SMALL_M;
-    // h as two bf16 planes (hi + lo): the down kernel is bound by weight bytes, so the
-    // extra activation bytes cost little and h is effectively not rounded.
-    p->h_dtype = SMLP_BF16_HILO;
-    p->h_bytes = round_up((size_t)(M * I) * 4, 256);
-    if (!plan_skinny(0, M, I, H, &p->gu) || !plan_skinny(1, M, H, I, &p->dn))
+    // h as one bf16 plane (rounded once, as the serving stack stores it) when the down
+    // contraction is long enough (I >= 256) for that rounding to average out and M <= 32
+    // (the projection kernel streams the down weights with a deeper LDS ring than the
+    // two-plane kernel has room for: 48.0 vs 51.5 us per Kimi-K3 layer at M = 16);
+    // otherwise two planes hi + lo, with which h is effectively not rounded.
+    const int hp = g_h_planes.load();
+    const bool one = hp == 1 || (hp == 0 && M <= 32 && I >= 256);
+    p->h_dtype = one ? SMLP_BF16 : SMLP_BF16_HILO;
+    p->h_bytes = round_up((size_t)(M * I) * (one ? 2 : 4), 256);
+    if (one && M > 32)
+      return fail(SMLP_ERR_ARG, "one plane of h on the small-M path needs M <= 32 (M = %lld)", (long long)M);
+    if (!plan_skinny(0, M, I, H, &p->gu) || !plan_skinny(1, M, H, I, &p->dn, one ? 2 : 1))
       return fail(SMLP_ERR_ARG, "the pinned small-M tuning is not a compiled configuration for M = %lld",
                   (long long)M);
     size_t part = 0;
@@ -670,6 +684,12 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
   g_tune[stage].waves = waves;
   g_tune[stage].u = u;
   g_tune[stage].ksplit = ksplit;
+  return ok();
+}
+
+int shared_mlp_tune_h_planes(int planes) {
+  if (planes < 0 || planes > 2) return fail(SMLP_ERR_ARG, "planes = %d outside {0, 1, 2}", planes);
+  g_h_planes = planes;
   return ok();
 }
 

@@ -650,6 +650,10 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
 }
 
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
+  if (p.h_dtype == SMLP_BF16)  // one plane of h: the plain projection out = h . Wd^T
+    return launch_skinny_linear(p.dn, static_cast<const char*>(ws) + p.h_offset, w_down, out, (int)p.M,
+                                (int)p.I, (int)p.H, (int)p.H, p.partial_fp32 ? 1 : 0,
+                                reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset), s);
   SkArgs a;
   const uint16_t* h = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.h_offset);
   a.a_hi = h;

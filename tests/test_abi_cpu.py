@@ -167,9 +167,30 @@ def test_stage_entry_points_validate(L):
 
 def test_workspace_and_plan(L):
     p = binding.shared_mlp_plan(16, H, I)
-    assert p["path_name"] == "small_m" and p["h_dtype"] == binding.SMLP_BF16_HILO
+    # decode: one bf16 plane of h; two planes (hi + lo) for a short down contraction,
+    # or on request
+    assert p["path_name"] == "small_m" and p["h_dtype"] == BF16
+    assert p["workspace_bytes"] >= 16 * I * 2
+    assert binding.shared_mlp_plan(16, H, 128)["h_dtype"] == binding.SMLP_BF16_HILO
     assert binding.shared_mlp_plan(8192, H, 128)["h_dtype"] == binding.SMLP_BF16_HILO
-    assert p["workspace_bytes"] >= 16 * I * 4
+    try:
+        binding.shared_mlp_tune_h_planes(2)
+        q = binding.shared_mlp_plan(16, H, I)
+        assert q["h_dtype"] == binding.SMLP_BF16_HILO and q["workspace_bytes"] >= 16 * I * 4
+        binding.shared_mlp_tune_h_planes(1)
+        assert binding.shared_mlp_plan(16, H, 128)["h_dtype"] == BF16
+        prev = binding.shared_mlp_set_large_m_threshold(129)
+        try:
+            with pytest.raises(binding.SmlpError):   # one plane: M <= 32 on the small path
+                binding.shared_mlp_plan(64, H, I)
+            binding.shared_mlp_tune_h_planes(0)
+            assert binding.shared_mlp_plan(64, H, I)["h_dtype"] == binding.SMLP_BF16_HILO
+        finally:
+            binding.shared_mlp_set_large_m_threshold(prev)
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_h_planes(3)
+    finally:
+        binding.shared_mlp_tune_h_planes(0)
     p = binding.shared_mlp_plan(8192, H, I)
     assert p["path_name"] == "large_m" and p["h_dtype"] == BF16
     assert p["workspace_bytes"] >= 8192 * I * 2

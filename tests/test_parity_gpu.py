@@ -89,6 +89,39 @@ def test_decode_replicated_m16(copy, x16):
     assert_rms_close(out, ref, BF16_TOL, f"rep M=16 copy{copy}")
 
 
+@pytest.mark.parametrize("planes", [1, 2])
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_decode_h_planes(M, planes):
+    # the small path with h forced to one bf16 plane or two (hi + lo); the default takes
+    # one plane here (I >= 256, M <= 32)
+    x = synth.activations(M, H, config=2, copy=M)
+    wgu, wd = synth.layer_weights(H, I, config=2, copy=3)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    try:
+        binding.shared_mlp_tune_h_planes(planes)
+        p = binding.shared_mlp_plan(M, H, I)
+        assert p["path_name"] == "small_m"
+        assert p["h_dtype"] == (binding.SMLP_BF16 if planes == 1 else binding.SMLP_BF16_HILO)
+        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
+    finally:
+        binding.shared_mlp_tune_h_planes(0)
+    assert_rms_close(out, ref, BF16_TOL, f"decode M={M} h planes={planes}")
+
+
+@pytest.mark.parametrize("Ii", [40, 128])
+def test_one_plane_short_contraction_forced(Ii):
+    # one plane of h forced where the default keeps two (I < 256): still within the bar
+    x = synth.activations(16, 1024, config=14, copy=Ii)
+    wgu, wd = synth.layer_weights(1024, Ii, config=14)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    try:
+        binding.shared_mlp_tune_h_planes(1)
+        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=True)
+    finally:
+        binding.shared_mlp_tune_h_planes(0)
+    assert_rms_close(out, ref, BF16_TOL, f"one plane forced I={Ii}")
+
+
 # -------------------------------------------------------------- TP8 shard, M = 128
 @pytest.mark.parametrize("copy", range(2))
 def test_tp8_shard_partial(copy):
