@@ -464,41 +464,57 @@ def main():
 
 
 def sweep(dev):
-    """M sweep {1..8192} for the replicated layer and the TP8 shard (8 / 16 copies cycled)."""
+    """M sweep {1..8192} for the replicated layer and the TP8 shard (8 / 16 weight copies
+    cycled, hipGraph replays), then the replicated-vs-sharded crossover that the measured
+    curves give under a model of the two collectives (include/smlp_layout.h)."""
     Ms = [1, 8, 32, 128, 512, 2048, 8192]
+    curves = {}
+    stream = torch.cuda.Stream(dev)
     for layout, I_r, partial, copies in (("replicated", I, False, 8), ("tp8", 768, True, 16)):
         weights = []
         for c in range(copies):
             wgu, wd = synth.layer_weights(H, I_r, config=6, copy=c, fan_in_down=I)
             weights.append((wgu.to(dev), wd.to(dev)))
+        pts = []
         for M in Ms:
             x = synth.activations(M, H, config=6, copy=M).to(dev)
             out = torch.empty(M, H, dtype=torch.float32 if partial else torch.bfloat16, device=dev)
             ws = torch.empty(max(binding.shared_mlp_workspace_bytes(M, H, I_r, 0), 256),
                              dtype=torch.uint8, device=dev)
-            steps = 200 if M <= 512 else 20
-            for i in range(5):
+
+            def fwd(i, st):
                 g, d = weights[i % copies]
-                binding.shared_mlp_forward(x, g, d, out, partial, ws)
+                binding.shared_mlp_forward(x, g, d, out, partial, ws, st)
+
+            with torch.cuda.stream(stream):
+                for i in range(copies):
+                    fwd(i, stream)
             torch.cuda.synchronize()
-            t0, t1 = _ev(), _ev()
-            t0.record()
-            for i in range(steps):
-                g, d = weights[i % copies]
-                binding.shared_mlp_forward(x, g, d, out, partial, ws)
-            t1.record()
-            torch.cuda.synchronize()
-            us = t0.elapsed_time(t1) * 1e3 / steps
+            us = _graph_time_us(stream, fwd, copies, max(1, (160 if M <= 512 else 16) // copies))
             alg = roofline.algorithmic_bytes(M, H, I_r, 2, 4 if partial else 2)
             fl = roofline.flops(M, H, I_r)
+            pts.append((M, us))
             print(json.dumps({"sweep": layout, "M": M, "I_r": I_r, "us_per_layer": round(us, 2),
                               "gbs": round(alg / us / 1e3, 1),
                               "hbm_frac": round(alg / us / 1e3 / roofline.HBM_PEAK_GBS, 4),
                               "tflops": round(fl / us / 1e6, 1),
                               "mfma_frac": round(fl / us / 1e6 / roofline.BF16_MFMA_PEAK_TFLOPS, 4),
-                              "path": binding.shared_mlp_plan(M, H, I_r, 0, partial)["path_name"]}),
+                              "path": binding.shared_mlp_plan(M, H, I_r, 0, partial)["path_name"],
+                              "launch": "hipGraph replay"}),
                   flush=True)
+        curves[layout] = ([float(m) for m, _ in pts], [u for _, u in pts])
         del weights
+    # crossover at TP8 over xGMI (7 links of ~153 GB/s per GPU); the fixed cost of one
+    # collective is not measured on one GPU, so the crossover is given for several values
+    alphas = [2.0, 5.0, 10.0, 20.0]
+    tc = []
+    for a in alphas:
+        m = binding.layout_model(8, H, curves["replicated"], curves["tp8"], a, 153.0, 7, 4)
+        tc.append(binding.shared_mlp_layout_crossover(m, 1 << 16))
+    print(json.dumps({"crossover": {"tp": 8, "link_gbps": 153.0, "links": 7, "partial": "fp32",
+                                    "alpha_us": alphas, "T_cross": tc,
+                                    "model": "shard while K_tp8(T) + AG(T) + RS(T) < K_rep(ceil(T/8))"}}),
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -61,6 +61,23 @@ EXPORTS = {
     "shared_mlp_restore_logical": (_int, [_vp, _vp, _i64, _i64, ctypes.POINTER(_i64), _int, _int, _int,
                                           _vp]),
 }
+
+
+class LayoutModel(ctypes.Structure):
+    _fields_ = [("tp", _int), ("hidden", _i64), ("partial_elem_bytes", _int), ("alpha_us", ctypes.c_double),
+                ("link_gbps", ctypes.c_double), ("links", _int),
+                ("n_rep", _int), ("rep_m", ctypes.POINTER(ctypes.c_double)), ("rep_us", ctypes.POINTER(ctypes.c_double)),
+                ("n_shard", _int), ("shard_m", ctypes.POINTER(ctypes.c_double)),
+                ("shard_us", ctypes.POINTER(ctypes.c_double))]
+
+
+_dp = ctypes.POINTER(ctypes.c_double)
+# declared in include/smlp_layout.h
+LAYOUT_EXPORTS = {
+    "shared_mlp_layout_times": (_int, [ctypes.POINTER(LayoutModel), _i64, _dp, _dp]),
+    "shared_mlp_choose_layout": (_int, [ctypes.POINTER(LayoutModel), _i64, ctypes.POINTER(_int)]),
+    "shared_mlp_layout_crossover": (_int, [ctypes.POINTER(LayoutModel), _i64, ctypes.POINTER(_i64)]),
+}
 # declared in include/smlp_tuning.h
 TUNING_EXPORTS = {
     "shared_mlp_tune_skinny": (_int, [_int, _int, _int, _int, _int, _int]),
@@ -77,7 +94,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m moe_shared_expert_amd.build` (no fallback exists)")
         L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in {**EXPORTS, **TUNING_EXPORTS}.items():
+        for name, (res, args) in {**EXPORTS, **TUNING_EXPORTS, **LAYOUT_EXPORTS}.items():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
@@ -287,3 +304,33 @@ def shared_mlp_restore_logical(gathered, out, sizes, tp: int, stream=None):
     _check(lib().shared_mlp_restore_logical(_ptr(gathered), _ptr(out), M, N, arr, len(sizes), int(tp), eb,
                                             _stream(stream, gathered.device)))
     return out
+
+
+def layout_model(tp, hidden, rep_curve, shard_curve, alpha_us, link_gbps, links=7, partial_elem_bytes=4):
+    """Build an smlp_layout_model; the returned object keeps the curve arrays alive."""
+    def arr(v):
+        return (ctypes.c_double * len(v))(*[float(a) for a in v])
+    keep = [arr(rep_curve[0]), arr(rep_curve[1]), arr(shard_curve[0]), arr(shard_curve[1])]
+    m = LayoutModel(int(tp), int(hidden), int(partial_elem_bytes), float(alpha_us), float(link_gbps), int(links),
+                    len(rep_curve[0]), ctypes.cast(keep[0], _dp), ctypes.cast(keep[1], _dp),
+                    len(shard_curve[0]), ctypes.cast(keep[2], _dp), ctypes.cast(keep[3], _dp))
+    m._keep = keep
+    return m
+
+
+def shared_mlp_layout_times(model, T: int):
+    r, s = ctypes.c_double(), ctypes.c_double()
+    _check(lib().shared_mlp_layout_times(ctypes.byref(model), int(T), ctypes.byref(r), ctypes.byref(s)))
+    return r.value, s.value
+
+
+def shared_mlp_choose_layout(model, T: int) -> bool:
+    v = _int()
+    _check(lib().shared_mlp_choose_layout(ctypes.byref(model), int(T), ctypes.byref(v)))
+    return bool(v.value)
+
+
+def shared_mlp_layout_crossover(model, T_max: int) -> int:
+    v = _i64()
+    _check(lib().shared_mlp_layout_crossover(ctypes.byref(model), int(T_max), ctypes.byref(v)))
+    return v.value

@@ -516,6 +516,14 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
 
 }  // namespace
 
+namespace smlp {
+// Status setter shared with the other host-only translation units (layout.cpp).
+int set_error(int status, const char* msg) {
+  if (status == SMLP_OK) return ok();
+  return fail(status, "%s", msg);
+}
+}  // namespace smlp
+
 extern "C" {
 
 const char* shared_mlp_status_string(int status) {

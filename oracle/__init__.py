@@ -1,5 +1,5 @@
-"""CPU fp64 oracle for the shared-expert SwiGLU MLP and the sharded MLA latent
-projection (test infrastructure).
+"""CPU fp64 oracle for the shared-expert SwiGLU MLP, the sharded MLA latent
+projection and the replicated-vs-sharded layout choice (test infrastructure).
 
 This package is test infrastructure. Only ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import it; the product path (the
@@ -30,3 +30,4 @@ from .mla_latent import (  # noqa: F401
     restore_logical,
     sharded_projection,
 )
+from . import layout  # noqa: F401

@@ -42,6 +42,13 @@ def test_every_declared_symbol_is_exported(L):
     for n in tuning:
         assert hasattr(L, n), n
     assert set(tuning) == set(binding.TUNING_EXPORTS)
+    layout = _declared("smlp_layout.h")
+    for n in layout:
+        assert hasattr(L, n), n
+    assert set(layout) == set(binding.LAYOUT_EXPORTS)
+    # every header under include/ is covered above
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(
+        ["smlp.h", "smlp_latent.h", "smlp_layout.h", "smlp_tuning.h"])
 
 
 def test_tuning_hook(L):
