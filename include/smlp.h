@@ -163,6 +163,22 @@ int shared_mlp_slice_rank(const void* w_gate_up, const void* w_down, void* w_gat
                           hipStream_t stream);
 
 /*
+ * Rank `rank`'s fp32 partial of the TP-sharded layer, computed straight from the full
+ * weights without copying a shard (the slice of shared_mlp_slice_rank, read in place):
+ * with s = I / tp, gate rows [r*s, (r+1)*s) and up rows I + [r*s, (r+1)*s) of w_gate_up
+ * [2I, H], and columns [r*s, (r+1)*s) of w_down [H, I] (row stride I).  Lets a caller
+ * that keeps the replicated weights resident run the sharded layout on any step.
+ *   x [M, H], out [M, H] fp32 (always the partial); workspace as for
+ *   shared_mlp_workspace_bytes(M, H, I / tp, dtype).  Requires I % tp == 0 and
+ *   0 <= rank < tp (else SMLP_ERR_ARG), and for bf16 s % 8 == 0 (SMLP_ERR_SHAPE).
+ * Equal, up to fp32 summation order, to shared_mlp_forward(partial_fp32 = 1) on the
+ * copied shard.
+ */
+int shared_mlp_forward_rank(const void* x, const void* w_gate_up, const void* w_down, void* out,
+                            int64_t M, int64_t H, int64_t I, int tp, int rank, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-token rescale to unit RMS, the glue between the layers of a stacked-layer
  * chain: out[m, :] = bf16_rne(in[m, :] / sqrt(mean_k in[m, k]^2)), computed in fp32.
  *   in   [M, H] fp32 (e.g. a partial output), out [M, H] bf16; no epsilon: a row

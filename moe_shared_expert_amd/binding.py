@@ -54,6 +54,7 @@ EXPORTS = {
     "shared_mlp_shard_eligible": (_int, [_int, _int, _int, _int, _i64, _i64]),
     "shared_mlp_slice_rank": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "shared_mlp_rms_rescale": (_int, [_vp, _vp, _i64, _i64, _vp]),
+    "shared_mlp_forward_rank": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _sz, _vp]),
     # declared in include/smlp_latent.h
     "shared_mlp_linear_plan": (_int, [_i64, _i64, _i64, ctypes.POINTER(_Plan)]),
     "shared_mlp_linear_workspace_bytes": (_int, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
@@ -334,3 +335,18 @@ def shared_mlp_layout_crossover(model, T_max: int) -> int:
     v = _i64()
     _check(lib().shared_mlp_layout_crossover(ctypes.byref(model), int(T_max), ctypes.byref(v)))
     return v.value
+
+
+def shared_mlp_forward_rank(x, w_gate_up, w_down, out, tp: int, rank: int, workspace=None, stream=None):
+    """Rank `rank`'s fp32 partial computed in place from the full weights (no shard copy)."""
+    M, H, I = _shapes(x, w_gate_up, w_down, out)
+    dt = _dtype_code(x)
+    if out.dtype != torch.float32:
+        raise TypeError("the rank partial is fp32")
+    if workspace is None:
+        need = shared_mlp_workspace_bytes(M, H, I // tp if tp > 0 and I % tp == 0 else I, dt)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(lib().shared_mlp_forward_rank(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), M, H, I, int(tp),
+                                         int(rank), dt, _ptr(workspace), workspace.numel(),
+                                         _stream(stream, x.device)))
+    return out

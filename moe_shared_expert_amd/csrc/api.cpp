@@ -349,6 +349,8 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
   p->h_offset = 0;
   p->part_offset = p->h_bytes;
   p->workspace_bytes = p->h_bytes + p->part_bytes;
+  p->up_off = I;
+  p->ldwd = I;
   return ok();
 }
 
@@ -691,6 +693,53 @@ int shared_mlp_restore_logical(const void* gathered, void* out, int64_t M, int64
   (void)hipGetLastError();
   rc = smlp::launch_restore_logical(gathered, out, M, n_gathered, sizes, nsizes, tp, elem_bytes, stream);
   if ((rc = hip_status(rc, "restore launch"))) return rc;
+  return ok();
+}
+
+int shared_mlp_forward_rank(const void* x, const void* w_gate_up, const void* w_down, void* out,
+                            int64_t M, int64_t H, int64_t I, int tp, int rank, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (tp < 1 || rank < 0 || rank >= tp || I < 1 || I % tp)
+    return fail(SMLP_ERR_ARG, "rank %d of tp %d does not slice I = %lld", rank, tp, (long long)I);
+  const int64_t sl = I / tp;
+  smlp::Plan p;
+  int rc = make_plan(M, H, sl, dtype, 1, &p);
+  if (rc) return rc;
+  if (2 * I * H >= kLimit) return fail(SMLP_ERR_SHAPE, "2*I*H must be < 2^31");
+  if (M == 0) return ok();
+  const size_t al = dtype == SMLP_BF16 ? 16 : 4, e = dtype == SMLP_BF16 ? 2 : 4;
+  if ((rc = check_ptr(x, "x", al)) || (rc = check_ptr(w_gate_up, "w_gate_up", al)) ||
+      (rc = check_ptr(w_down, "w_down", al)) || (rc = check_ptr(out, "out", al)) ||
+      (rc = check_ptr(workspace, "workspace", 256)))
+    return rc;
+  if (workspace_bytes < p.workspace_bytes)
+    return fail(SMLP_ERR_WORKSPACE, "workspace_bytes = %zu < %zu needed", workspace_bytes, p.workspace_bytes);
+  const size_t x_n = (size_t)(M * H) * e, wgu_n = (size_t)(2 * I * H) * e, wd_n = (size_t)(H * I) * e,
+               out_n = (size_t)(M * H) * 4, ws_n = p.workspace_bytes;
+  if (overlap(workspace, ws_n, x, x_n) || overlap(workspace, ws_n, w_gate_up, wgu_n) ||
+      overlap(workspace, ws_n, w_down, wd_n) || overlap(out, out_n, x, x_n) ||
+      overlap(out, out_n, w_gate_up, wgu_n) || overlap(out, out_n, w_down, wd_n) ||
+      overlap(out, out_n, workspace, ws_n))
+    return fail(SMLP_ERR_ALIAS, "out or the workspace overlaps an input (or each other)");
+  // The rank's slice, read in place: gate rows [r s, (r+1) s) with their up rows I rows
+  // further on, and the K range [r s, (r+1) s) of every w_down row (row stride I).
+  p.up_off = I;
+  p.ldwd = I;
+  const char* gu = static_cast<const char*>(w_gate_up) + (size_t)rank * sl * H * e;
+  const char* wd = static_cast<const char*>(w_down) + (size_t)rank * sl * e;
+  (void)hipGetLastError();
+  switch (p.path) {
+    case SMLP_PATH_FP32: rc = smlp::launch_fp32_gate_up(p, (const float*)x, (const float*)gu, workspace, stream); break;
+    case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_gate_up(p, x, gu, workspace, stream); break;
+    default: rc = smlp::launch_gemm_gate_up(p, x, gu, workspace, stream); break;
+  }
+  if ((rc = hip_status(rc, "gate_up launch"))) return rc;
+  switch (p.path) {
+    case SMLP_PATH_FP32: rc = smlp::launch_fp32_down(p, (const float*)wd, (float*)out, workspace, stream); break;
+    case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_down(p, wd, out, workspace, stream); break;
+    default: rc = smlp::launch_gemm_down(p, wd, out, workspace, stream); break;
+  }
+  if ((rc = hip_status(rc, "down launch"))) return rc;
   return ok();
 }
 

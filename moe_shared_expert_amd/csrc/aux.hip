@@ -9,14 +9,15 @@ namespace smlp {
 // h[m, i] = SiLU(sum_k x[m,k] Wg[i,k]) * (sum_k x[m,k] Wu[i,k]), fp32, one thread per (m, i).
 __global__ __launch_bounds__(256) void fp32_gate_up_kernel(const float* __restrict__ x,
                                                            const float* __restrict__ w, int M,
-                                                           int H, int I, float* __restrict__ h) {
+                                                           int H, int I, int up_off,
+                                                           float* __restrict__ h) {
   const size_t total = (size_t)M * I;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
     const size_t m = e / I, i = e % I;
     const float* xr = x + m * H;
     const float* gr = w + i * H;
-    const float* ur = w + ((size_t)I + i) * H;
+    const float* ur = w + ((size_t)up_off + i) * H;
     float g = 0.f, u = 0.f;
     for (int k = 0; k < H; ++k) {
       g = fmaf(xr[k], gr[k], g);
@@ -29,13 +30,14 @@ __global__ __launch_bounds__(256) void fp32_gate_up_kernel(const float* __restri
 // out[m, n] = sum_i h[m, i] Wd[n, i], fp32, one thread per (m, n).
 __global__ __launch_bounds__(256) void fp32_down_kernel(const float* __restrict__ h,
                                                         const float* __restrict__ wd, int M,
-                                                        int H, int I, float* __restrict__ out) {
+                                                        int H, int I, int ldw,
+                                                        float* __restrict__ out) {
   const size_t total = (size_t)M * H;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
     const size_t m = e / H, n = e % H;
     const float* hr = h + m * I;
-    const float* wr = wd + n * I;
+    const float* wr = wd + n * ldw;
     float acc = 0.f;
     for (int i = 0; i < I; ++i) acc = fmaf(hr[i], wr[i], acc);
     out[e] = acc;
@@ -51,14 +53,14 @@ int launch_fp32_gate_up(const Plan& p, const float* x, const float* w_gate_up, v
                         hipStream_t s) {
   float* h = reinterpret_cast<float*>(static_cast<char*>(ws) + p.h_offset);
   hipLaunchKernelGGL(fp32_gate_up_kernel, dim3(grid_for((size_t)p.M * p.I)), dim3(256), 0, s, x,
-                     w_gate_up, (int)p.M, (int)p.H, (int)p.I, h);
+                     w_gate_up, (int)p.M, (int)p.H, (int)p.I, (int)p.up_off, h);
   return (int)hipGetLastError();
 }
 
 int launch_fp32_down(const Plan& p, const float* w_down, float* out, void* ws, hipStream_t s) {
   const float* h = reinterpret_cast<const float*>(static_cast<const char*>(ws) + p.h_offset);
   hipLaunchKernelGGL(fp32_down_kernel, dim3(grid_for((size_t)p.M * p.H)), dim3(256), 0, s, h,
-                     w_down, (int)p.M, (int)p.H, (int)p.I, out);
+                     w_down, (int)p.M, (int)p.H, (int)p.I, (int)p.ldwd, out);
   return (int)hipGetLastError();
 }
 

@@ -46,6 +46,7 @@ struct GArgs {
   int N;                  // output features: h columns (gate_up) or H (down)
   int up_off;             // gate_up: first up row (= I)
   int b_rows;             // rows of b
+  int ldb;                // elements between consecutive rows of b (>= K)
   int tiles_m, tiles_n;
   int kslice;             // K elements per workgroup slice (gridDim.y slices)
   void* out;              // gate_up: h plane(s); down: out [M, N] bf16 or fp32
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   const int nk = (kend - kbeg + BK - 1) / BK;
 
   const uint32_t abytes = (uint32_t)g.M * (uint32_t)K * 2u;
-  const uint32_t bbytes = (uint32_t)g.b_rows * (uint32_t)K * 2u;
+  const uint32_t bbytes = ((uint32_t)(g.b_rows - 1) * (uint32_t)g.ldb + (uint32_t)K) * 2u;
   const __amdgpu_buffer_rsrc_t arsc[2] = {make_rsrc(g.a, abytes), make_rsrc(NA == 2 ? g.a_lo : g.a, abytes)};
   const __amdgpu_buffer_rsrc_t brsc = make_rsrc(g.b, bbytes);
 
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
       row = tile_n * BN + r;
       ok = row < g.N;
     }
-    boff[i] = ok ? (uint32_t)row * (uint32_t)K * 2u + bchk[i] * 16 : bbytes;
+    boff[i] = ok ? (uint32_t)row * (uint32_t)g.ldb * 2u + bchk[i] * 16 : bbytes;
   }
 
   f32x16 acc[TM][TN];
@@ -357,8 +358,9 @@ int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, voi
   a.M = (int)p.M;
   a.K = (int)p.H;
   a.N = (int)p.I;
-  a.up_off = (int)p.I;
-  a.b_rows = (int)(2 * p.I);
+  a.up_off = (int)p.up_off;
+  a.b_rows = (int)(p.up_off + p.I);
+  a.ldb = (int)p.H;
   a.tiles_m = p.ggu.tiles_m;
   a.tiles_n = p.ggu.tiles / p.ggu.tiles_m;
   a.kslice = p.ggu.kslice;
@@ -383,6 +385,7 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
   a.N = (int)p.H;
   a.up_off = 0;
   a.b_rows = (int)p.H;
+  a.ldb = (int)p.ldwd;
   a.tiles_m = p.gdn.tiles_m;
   a.tiles_n = p.gdn.tiles / p.gdn.tiles_m;
   a.kslice = p.gdn.kslice;
@@ -409,6 +412,7 @@ int launch_gemm_linear(const GemmPlan& gp, const void* x, const void* w, void* y
   a.N = N;
   a.up_off = 0;
   a.b_rows = N;
+  a.ldb = K;
   a.tiles_m = gp.tiles_m;
   a.tiles_n = gp.tiles / gp.tiles_m;
   a.kslice = gp.kslice;

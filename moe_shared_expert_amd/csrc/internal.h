@@ -47,6 +47,10 @@ struct Plan {
   SkinnyPlan gu, dn;
   GemmPlan ggu, gdn;
   int kernels;
+  // Weight views (a rank's slice read in place from full weights): rows between a gate
+  // row and its up row in w_gate_up (I for whole weights), and the row stride of w_down
+  // in elements (I for whole weights).
+  int64_t up_off, ldwd;
 };
 
 // Weight-streaming stages (skinny.hip).  Return a hipError_t.
@@ -64,7 +68,7 @@ int launch_finalize(bool gate_up, const float* part, int ksplit, int M, int N, v
 // the streaming kernel (plan kind SKINNY_STREAM16, M <= 32) or the LDS-tiled kernel,
 // with `part` holding ksplit x M x N fp32 partials when the plan splits K.
 int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, void* y, int M, int K,
-                         int N, int ldy, int out_f32, float* part, hipStream_t s);
+                         int N, int ldy, int out_f32, float* part, hipStream_t s, int ldw = 0);
 int launch_gemm_linear(const GemmPlan& gp, const void* x, const void* w, void* y, int M, int K,
                        int N, int ldy, int out_f32, float* part, hipStream_t s);
 // Rank-major -> logical column order of a gathered merged-column output (latent.hip);

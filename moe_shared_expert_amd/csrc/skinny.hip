@@ -50,6 +50,7 @@ struct SkArgs {
   int h_planes;          // gate_up (and its finalize): h planes to store, 2 on this path
   int fpw;               // LDS kernel: features (gate_up) or rows (down) per workgroup
   int w_rows;            // rows of w
+  int ldw;               // elements between consecutive rows of w (>= K)
 };
 
 // Store element (m, n) of h: rne(h) in the first plane and, with two planes, the
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   }
   const int f0 = col * a.fpw;
   const int fend = min(a.N, f0 + a.fpw);
-  const uint32_t wbytes = (uint32_t)a.w_rows * (uint32_t)K * 2u;
+  const uint32_t wbytes = ((uint32_t)(a.w_rows - 1) * (uint32_t)a.ldw + (uint32_t)K) * 2u;
   const uint32_t abytes = (uint32_t)a.M * (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, wbytes);
   const __amdgpu_buffer_rsrc_t ar[2] = {make_rsrc(a.a_hi, abytes), make_rsrc(NA == 2 ? a.a_lo : a.a_hi, abytes)};
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
         row = f0 + 16 * t + 8 * h + lr;
         ok = row < fend;
       }
-      wo[t][h] = ok ? (uint32_t)row * (uint32_t)K * 2u + ch[h] * 16 : wbytes;
+      wo[t][h] = ok ? (uint32_t)row * (uint32_t)a.ldw * 2u + ch[h] * 16 : wbytes;
     }
 #pragma unroll
   for (int q = 0; q < NA; ++q)
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_direct_kernel(SkArgs a) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int row = p ? a.up_off + n : n;
-      wrow[p][nb] = reinterpret_cast<const char*>(a.w) + ((size_t)row * K + lg * 8) * 2;
+      wrow[p][nb] = reinterpret_cast<const char*>(a.w) + ((size_t)row * a.ldw + lg * 8) * 2;
     }
   }
   const char* arow[NA][MT];
@@ -635,7 +636,7 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.M = (int)p.M;
   a.K = (int)p.H;
   a.N = (int)p.I;
-  a.up_off = (int)p.I;
+  a.up_off = (int)p.up_off;
   a.kslice = p.gu.kslice;
   a.out = static_cast<char*>(ws) + p.h_offset;
   a.ldo = a.N;
@@ -643,7 +644,8 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.out_f32 = 0;
   a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
   a.fpw = p.gu.fpw;
-  a.w_rows = (int)(2 * p.I);
+  a.w_rows = (int)(p.up_off + p.I);
+  a.ldw = (int)p.H;
   int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
   if (rc || p.gu.ksplit == 1) return rc;
   return launch_finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);
@@ -653,7 +655,8 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   if (p.h_dtype == SMLP_BF16)  // one plane of h: the plain projection out = h . Wd^T
     return launch_skinny_linear(p.dn, static_cast<const char*>(ws) + p.h_offset, w_down, out, (int)p.M,
                                 (int)p.I, (int)p.H, (int)p.H, p.partial_fp32 ? 1 : 0,
-                                reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset), s);
+                                reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset), s,
+                                (int)p.ldwd);
   SkArgs a;
   const uint16_t* h = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.h_offset);
   a.a_hi = h;
@@ -671,13 +674,14 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
   a.fpw = p.dn.fpw;
   a.w_rows = (int)p.H;
+  a.ldw = (int)p.ldwd;
   int rc = launch_stage<MODE_DOWN_HILO>(p.dn, a, s);
   if (rc || p.dn.ksplit == 1) return rc;
   return launch_finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.N, a.out_f32, 1, s);
 }
 
 int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, void* y, int M, int K,
-                         int N, int ldy, int out_f32, float* part, hipStream_t s) {
+                         int N, int ldy, int out_f32, float* part, hipStream_t s, int ldw) {
   SkArgs a;
   a.a_hi = reinterpret_cast<const uint16_t*>(x);
   a.a_lo = nullptr;
@@ -694,6 +698,7 @@ int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, voi
   a.h_planes = 1;
   a.fpw = sp.fpw;
   a.w_rows = N;
+  a.ldw = ldw > 0 ? ldw : K;
   int rc = launch_stage<MODE_LINEAR>(sp, a, s);
   if (rc || sp.ksplit == 1) return rc;
   return launch_finalize(false, part, sp.ksplit, M, N, y, ldy, out_f32, 1, s);

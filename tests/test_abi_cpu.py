@@ -258,3 +258,20 @@ def test_rescale_validation(L):
     assert r(X + 4, OUT, 128, H, None) == 3
     assert r(X, X + 64, 128, H, None) == 4
     assert r(None, None, 0, H, None) == 0
+
+
+def test_forward_rank_validation(L):
+    # every call below fails validation on the host (none may reach a launch)
+    ws = _ws(16, H, I // 8)
+    f = lambda **k: L.shared_mlp_forward_rank(k.get("x", X), k.get("g", WGU), k.get("d", WD), k.get("o", OUT),
+                                              k.get("m", 16), H, k.get("i", I), k.get("tp", 8), k.get("r", 0),
+                                              k.get("dt", BF16), k.get("ws", WS), k.get("wsb", ws), None)
+    assert f(tp=0) == 8 and f(tp=7) == 8 and f(r=8) == 8 and f(r=-1) == 8     # SMLP_ERR_ARG
+    assert f(i=6152, tp=8) == 2                    # the bf16 slice 769 is not a multiple of 8
+    assert f(i=8 * 12, tp=8) == 2                  # bf16 slice of 12 is not a multiple of 8
+    assert f(x=0) == 1 and f(o=0) == 1 and f(ws=0) == 1
+    assert f(d=WD + 8) == 3
+    assert f(wsb=ws - 1) == 5
+    assert f(o=WD + 64) == 4 and f(ws=X) == 4
+    assert f(dt=5) == 6
+    assert L.shared_mlp_forward_rank(None, None, None, None, 0, H, I, 8, 0, BF16, None, 0, None) == 0

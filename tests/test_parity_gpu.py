@@ -409,3 +409,57 @@ def test_graph_replays_match_eager(M, partial):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(ibits), eager.view(ibits)), f"replay {rep}"
+
+
+# ------------------------------------------- rank partial read in place from full weights
+@pytest.mark.parametrize("M", [1, 16, 32, 64, 128, 300])
+@pytest.mark.parametrize("tp", [8, 16])
+def test_forward_rank_in_place(M, tp):
+    # the sharded layout run on views of the replicated weights (no shard copy): each
+    # rank's partial against the oracle's, on every path the planner takes for these M
+    Hh, Ii = 1024, 2048
+    x = synth.activations(M, Hh, config=15, copy=M)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=15)
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+    for r in sorted({0, 1, tp - 1}):
+        out = torch.full((M, Hh), float("nan"), dtype=torch.float32, device=DEV)
+        binding.shared_mlp_forward_rank(xd, gd, dd, out, tp, r)
+        torch.cuda.synchronize()
+        ref = oracle.rank_partial(f64(x), f64(wgu), f64(wd), tp, r)
+        assert_rms_close(out, ref, BF16_TOL, f"rank in place M={M} tp={tp} r={r}")
+
+
+def test_forward_rank_matches_copied_shard_and_sums():
+    # Kimi-K3 shapes, TP8, M = 128: in place equals the copied shard up to summation
+    # order, and the 8 partials sum to the replicated output
+    x = synth.activations(128, H, config=16)
+    wgu, wd = synth.layer_weights(H, I, config=16)
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+    total = np.zeros((128, H))
+    for r in range(8):
+        a = torch.empty(128, H, dtype=torch.float32, device=DEV)
+        binding.shared_mlp_forward_rank(xd, gd, dd, a, 8, r)
+        g_r, d_r = slice_on_gpu(gd, dd, 8, r)
+        b = run_forward(xd, g_r, d_r, partial=True)
+        ref_r = oracle.rank_partial(f64(x), f64(wgu), f64(wd), 8, r)
+        assert_rms_close(a, ref_r, BF16_TOL, f"rank {r} in place")
+        assert_rms_close(a, f64(b), BF16_TOL, f"rank {r} in place vs copied")
+        total += f64(a)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(torch.from_numpy(total), ref, BF16_TOL, "sum of in-place partials")
+
+
+def test_forward_rank_fp32_tiny():
+    x, gate, up, down, tp, t = synth.tiny_fp32_case()
+    wgu = synth.merged_gate_up(gate, up)
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), down.to(DEV)
+    total = np.zeros((12, 16))
+    for r in range(tp):
+        out = torch.empty(12, 16, dtype=torch.float32, device=DEV)
+        binding.shared_mlp_forward_rank(xd, gd, dd, out, tp, r)
+        torch.cuda.synchronize()
+        ref_r = oracle.rank_partial(f64(x), f64(wgu), f64(down), tp, r)
+        assert_rms_close(out, ref_r, FP32_TOL, f"tiny fp32 rank {r} in place")
+        total += f64(out)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(down))
+    assert np.abs(total - ref).max() <= FP32_TOL * rms(ref)
