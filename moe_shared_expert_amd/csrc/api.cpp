@@ -100,10 +100,27 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
   const int64_t ksteps = (K + 63) / 64;
   if (sp.kind == SKINNY_STREAM16) {
     const int64_t tile = stage == 0 ? 8 : 16;  // features per 16-row tile
+    // Short TP shards (measured on MI355X, H = 7168): gate_up with few features (I_r <= 512,
+    // or I_r < 2048 at 17-32 tokens) fills whole tiles, ~48 workgroup columns, and splits
+    // K four ways (I_r = 384, M = 16: 8.6 -> 7.7 us; I_r = 768, M = 32: 13.4 -> 11.7 us)
+    // instead of spreading a few features over every compute unit; the one-plane down
+    // stage with a short K (<= 1024) takes two whole tiles per workgroup with 4 waves and
+    // 4 stages (I_r = 768: 6.0 -> 5.5 us; I_r = 384: 4.9 -> 4.5 us).
+    const bool auto_shape = !o.nb.load() && !o.ksplit.load() && !o.waves.load() && !o.u.load();
+    const bool gu_split = auto_shape && stage == 0 && N < tile * kCUs && (sp.mt == 2 || N <= 512);
+    const bool dn_short = auto_shape && stage == 1 && inst == 2 && K <= 1024 && N >= 2048;
     int64_t groups = o.nb.load() ? (N + tile * o.nb.load() - 1) / (tile * o.nb.load()) : kCUs;
     if (groups > N) groups = N;
     int64_t fpw = (N + groups - 1) / groups;
     int64_t nt = (fpw + tile - 1) / tile;
+    if (gu_split) {
+      nt = (N + 24 * tile) / (48 * tile);  // round(N / (48 * tile)): about 48 columns
+      nt = nt < 1 ? 1 : nt > 4 ? 4 : nt;
+      fpw = nt * tile;
+    } else if (dn_short) {
+      nt = 2;
+      fpw = 2 * tile;
+    }
     if (nt > 4) {
       nt = 4;
       fpw = 4 * tile;
@@ -119,7 +136,10 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     static const int kPrefDN1[][2] = {{8, 3}, {4, 4}, {8, 2}, {4, 6}};
     const int (*pref)[2] = stage == 0 ? kPrefGU : inst == 2 ? kPrefDN1 : kPrefDN;
     const int npref = stage == 0 ? 4 : inst == 2 ? 4 : 5;
-    if (!o.waves.load() || !o.u.load()) {
+    if ((gu_split || dn_short) && smlp::skinny_instantiated(inst, sp.kind, sp.mt, (int)nt, 4, 4)) {
+      sp.waves = 4;
+      sp.u = 4;
+    } else if (!o.waves.load() || !o.u.load()) {
       for (int c = 0; c < npref; ++c) {
         const int w = o.waves.load() ? o.waves.load() : pref[c][0];
         const int st = o.u.load() ? o.u.load() : pref[c][1];
@@ -132,7 +152,7 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     }
     if (o.waves.load()) sp.waves = o.waves.load();
     if (o.u.load()) sp.u = o.u.load();
-    int64_t ks = o.ksplit.load() ? o.ksplit.load() : 1;
+    int64_t ks = o.ksplit.load() ? o.ksplit.load() : gu_split ? 4 : 1;
     if (ks > ksteps) ks = ksteps;
     const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
     ks = (K + kslice - 1) / kslice;
