@@ -493,8 +493,8 @@ template <bool GU>
 __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__ part,
                                                        int ksplit, int M, int N, void* out,
                                                        int ldo, int out_f32, int h_planes) {
-  // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, four
-  // slices in flight at a time, summed in slice order.  Down and projection outputs
+  // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, up to
+  // eight slices in flight at a time, summed in slice order.  Down and projection outputs
   // have row stride ldo (a multiple of 4).
   constexpr int P = GU ? 2 : 1;
   const int N4 = N >> 2;
@@ -505,23 +505,24 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
     const int m = (int)(e / N4), n = (int)(e % N4) * 4;
     const float* base = part + (size_t)m * P * N + n;
     f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 4 <= ksplit; s += 4) {
-      f32x4 a[4], b[4];
+    // Eight slices per batch, all loads of a batch in flight together (the last batch
+    // takes the remaining slices), summed in slice order.
+    for (int s = 0; s < ksplit; s += 8) {
+      f32x4 a[8], b[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride);
-        if (GU) b[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride + N);
+      for (int q = 0; q < 8; ++q) {
+        if (s + q < ksplit) {
+          a[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride);
+          if (GU) b[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride + N);
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        g += a[q];
-        if (GU) u += b[q];
+      for (int q = 0; q < 8; ++q) {
+        if (s + q < ksplit) {
+          g += a[q];
+          if (GU) u += b[q];
+        }
       }
-    }
-    for (; s < ksplit; ++s) {
-      g += *reinterpret_cast<const f32x4*>(base + (size_t)s * sstride);
-      if (GU) u += *reinterpret_cast<const f32x4*>(base + (size_t)s * sstride + N);
     }
     const size_t o = (size_t)m * (GU ? N : ldo) + n;
     if (GU) {

@@ -463,3 +463,25 @@ def test_forward_rank_fp32_tiny():
         total += f64(out)
     ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(down))
     assert np.abs(total - ref).max() <= FP32_TOL * rms(ref)
+
+
+def test_largest_legal_token_count():
+    # M * H = 2^31 - 1 - (2^31 - 1) % H, the largest the 32-bit buffer offsets allow (H = I = 256):
+    # x is a seeded 4096-row block repeated on the device; sampled rows against the oracle,
+    # including the last row
+    Hh = Ii = 256
+    M = (2 ** 31 - 1) // Hh
+    block = synth.activations(4096, Hh, config=19)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=19)
+    print(f"largest M = {M}", flush=True)
+    x = block.to(DEV).repeat((M + 4095) // 4096, 1)[:M].contiguous()
+    p = binding.shared_mlp_plan(M, Hh, Ii)
+    assert p["path_name"] == "large_m"
+    out = run_forward(x, wgu.to(DEV), wd.to(DEV))
+    rows = [0, 1, 4095, 4096, M // 2, M - 4097, M - 2, M - 1]
+    got = out[rows].cpu()
+    del x, out
+    torch.cuda.empty_cache()
+    ref_all = oracle.swiglu_mlp(f64(block), f64(wgu), f64(wd))
+    ref = ref_all[[r % 4096 for r in rows]]
+    assert_rms_close(got, ref, BF16_TOL, f"largest M={M}", ref_rms=rms(ref_all))
