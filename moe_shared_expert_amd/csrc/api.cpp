@@ -75,12 +75,14 @@ struct GemmOverride {
 };
 GemmOverride g_gtune[3];
 
-// Planes of h on the small-M path (0 = automatic: two), see shared_mlp_tune_h_planes.
+// Planes of h on the small-M path (0 = automatic: one for M <= 32 and I >= 256, else
+// two), see shared_mlp_tune_h_planes.
 std::atomic<int> g_h_planes{0};
 
 // Small-M stage plan.  M <= 32: the streaming kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
-// range, waves interleaved over K.  M > 32: the direct-load kernel over 16-feature
+// range, waves interleaved over K (short TP shards: whole tiles and a K split, below).
+// M > 32: the direct-load kernel over 16-feature
 // blocks, with a K split over workgroups when the blocks alone cannot keep about
 // three waves per compute unit streaming.  Returns false if a pinned (tuned)
 // configuration is not one of the compiled kernels.
@@ -129,8 +131,8 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     sp.nb = (int)nt;
     sp.fpw = (int)fpw;
     // Measured on MI355X: gate_up is fastest with 4 waves and a 3-stage ring, down
-    // with 8 waves and 2 stages; otherwise the first compiled (waves, stages) pair in
-    // this order.
+    // with 8 waves and 2 stages (two planes of h) or 3 stages (one plane); otherwise
+    // the first compiled (waves, stages) pair in this order.
     static const int kPrefGU[][2] = {{4, 3}, {4, 4}, {4, 2}, {8, 2}};
     static const int kPrefDN[][2] = {{8, 2}, {8, 3}, {4, 4}, {4, 3}, {4, 2}};
     static const int kPrefDN1[][2] = {{8, 3}, {4, 4}, {8, 2}, {4, 6}};

@@ -23,9 +23,12 @@
 // feature blocks) is reduced by a second, elementwise kernel that also applies the
 // epilogue.
 //
-// The intermediate h is handed from gate_up to down as two bf16 planes, hi = rne(h)
-// and lo = rne(h - hi), which together carry ~16 significant bits; the down kernel
-// multiplies both (two MFMAs per fragment), so h is effectively not rounded.
+// The intermediate h is handed from gate_up to down either as one bf16 plane (rounded
+// once; the down stage is then the one-plane projection mode) or as two bf16 planes,
+// hi = rne(h) and lo = rne(h - hi), which together carry ~16 significant bits; with
+// two planes the down kernel multiplies both (two MFMAs per fragment), so h is
+// effectively not rounded.  The planner picks one plane unless the down contraction
+// is short.
 #include "device_common.h"
 #include "internal.h"
 #include "smlp.h"
@@ -47,7 +50,7 @@ struct SkArgs {
   int ldo;               // down / projection: elements between output rows (>= N)
   float* part;           // ksplit > 1: partial sums [ksplit][M][P*N]
   int out_f32;           // down: fp32 (1) or bf16 (0) output
-  int h_planes;          // gate_up (and its finalize): h planes to store, 2 on this path
+  int h_planes;          // gate_up (and its finalize): h planes to store (1 or 2)
   int fpw;               // LDS kernel: features (gate_up) or rows (down) per workgroup
   int w_rows;            // rows of w
   int ldw;               // elements between consecutive rows of w (>= K)
