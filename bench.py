@@ -338,23 +338,33 @@ KERNEL_SOURCES = ("moe_shared_expert_amd/csrc/skinny.hip", "moe_shared_expert_am
                   "moe_shared_expert_amd/csrc/device_common.h", "moe_shared_expert_amd/csrc/api.cpp")
 
 
+def kernel_source_hash():
+    """SHA-256 (16 hex digits) of the kernel sources with comments and whitespace removed,
+    so that a profile summary stays valid across comment-only edits."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        src = open(os.path.join(ROOT, f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
+
+
 def profiled_traffic(name):
     """HBM bytes per launch of the dominant kernel (gate_up, or the latent projection)
     from the committed rocprofv3 counter summary of this workload
     (profiles/<workload>.md), or None when that summary was taken on different kernel
     sources than the ones built now."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"{name}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
     m = re.search(r"kernel source hash[^`]*`([0-9a-f]+)`", text)
     t = re.search(r"(?:gate_up|projection) traffic bytes per launch: (\d+)", text)
-    if not m or not t or m.group(1) != h.hexdigest()[:16]:
+    if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return int(t.group(1))
 
