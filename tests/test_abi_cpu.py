@@ -275,3 +275,26 @@ def test_forward_rank_validation(L):
     assert f(o=WD + 64) == 4 and f(ws=X) == 4
     assert f(dt=5) == 6
     assert L.shared_mlp_forward_rank(None, None, None, None, 0, H, I, 8, 0, BF16, None, 0, None) == 0
+
+
+def test_last_error_is_per_thread(L):
+    # each thread sees the detail of its own last failure (both calls fail validation on
+    # the host: thread 0 an unknown dtype, thread 1 a misaligned x)
+    import threading
+    seen = {0: set(), 1: set()}
+
+    def worker(k):
+        for _ in range(200):
+            if k == 0:
+                rc = L.shared_mlp_forward(X, WGU, WD, OUT, 16, H, I, 7, 0, WS, 1 << 40, None)
+            else:
+                rc = L.shared_mlp_forward(X + 8, WGU, WD, OUT, 16, H, I, BF16, 0, WS, 1 << 40, None)
+            seen[k].add((rc, L.shared_mlp_last_error().decode().split(" ")[0]))
+
+    ts = [threading.Thread(target=worker, args=(k,)) for k in (0, 1)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert seen[0] == {(6, "dtype")}, seen[0]
+    assert seen[1] == {(3, "x")}, seen[1]

@@ -485,3 +485,26 @@ def test_largest_legal_token_count():
     ref_all = oracle.swiglu_mlp(f64(block), f64(wgu), f64(wd))
     ref = ref_all[[r % 4096 for r in rows]]
     assert_rms_close(got, ref, BF16_TOL, f"largest M={M}", ref_rms=rms(ref_all))
+
+
+def test_concurrent_streams_match_sequential():
+    # calls with their own workspaces on two streams share no device state: run together,
+    # every output equals its sequential result bit for bit
+    xa = synth.activations(16, H, config=2, copy=5).to(DEV)
+    ga, da = (t.to(DEV) for t in synth.layer_weights(H, I, config=2, copy=5))
+    xb = synth.activations(128, H, config=3, copy=5).to(DEV)
+    gb, db = (t.to(DEV) for t in synth.layer_weights(H, 768, config=3, copy=5, fan_in_down=I))
+    ref_a = run_forward(xa, ga, da)
+    ref_b = run_forward(xb, gb, db, partial=True)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    wsa, wsb = workspace_for(16, H, I, binding.SMLP_BF16), workspace_for(128, H, 768, binding.SMLP_BF16)
+    outs_a = [torch.full((16, H), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(6)]
+    outs_b = [torch.full((128, H), float("nan"), dtype=torch.float32, device=DEV) for _ in range(6)]
+    torch.cuda.synchronize()
+    for i in range(6):
+        binding.shared_mlp_forward(xa, ga, da, outs_a[i], False, wsa, sa)
+        binding.shared_mlp_forward(xb, gb, db, outs_b[i], True, wsb, sb)
+    torch.cuda.synchronize()
+    for i in range(6):
+        assert torch.equal(outs_a[i].view(torch.int16), ref_a.view(torch.int16)), i
+        assert torch.equal(outs_b[i], ref_b), i
