@@ -3,10 +3,11 @@
  * expert (host-only functions of libsmlp.so; no HIP call).
  *
  * vLLM PR 50656, "[Kimi-K3] Add option to shard the shared expert instead of
- * replicating": sharding trades weight bandwidth for two collectives per layer (an
- * all-gather of the tokens before the MLP and a reduce-scatter of the partial outputs
- * after it, section "Change"); it wins only at low token counts, and one global flag
- * cannot suit both prefill and decode (section "Trade-off and why it is opt-in"); the
+ * replicating": a sharded rank reads a 1/tp slice of the weights but adds two
+ * collectives to every layer (an all-gather of the tokens before the MLP and a
+ * reduce-scatter of the partial outputs after it, section "Change"); that pays off for
+ * small token counts only, so one process-wide switch is wrong for either prefill or
+ * decode (section "Trade-off and why it is opt-in"); the
  * crossover is an estimate, about 700 tokens at TP8 on the authors' hardware (section
  * "Evaluation").  These functions make the choice per step from measured kernel-time
  * curves and a model of the two collectives:

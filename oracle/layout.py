@@ -6,8 +6,9 @@ CPU-baseline leg of bench.py. It shares no code with the HIP library.
 Source (cited as [PR50656 section]): vLLM PR 50656, "[Kimi-K3] Add option to shard the
 shared expert instead of replicating" -- sections "Change" (an all-gather of the tokens
 before the sharded MLP and a reduce-scatter of its partial outputs after it), "Trade-off
-and why it is opt-in" (sharding trades weight bandwidth for two collectives per layer and
-wins only at low token counts; one global flag cannot suit both prefill and decode) and
+and why it is opt-in" (a sharded rank reads a 1/tp slice of the weights but adds an
+all-gather and a reduce-scatter to every layer, which pays off for small token counts only,
+so a single process-wide switch is wrong for either prefill or decode) and
 "Evaluation" (the crossover is estimated, about 700 tokens at TP8, not measured).
 
 The model, for one step of T tokens spread over tp ranks (sequence parallel):

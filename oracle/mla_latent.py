@@ -37,8 +37,8 @@ def _f64(a: np.ndarray, name: str) -> np.ndarray:
 
 
 def check_geometry(sizes: Sequence[int], tp: int) -> None:
-    """Reject range sizes that are not positive multiples of tp ([PR345 Compatibility]:
-    every merged output size must be divisible by the tensor-parallel size)."""
+    """Reject range sizes that are not positive multiples of tp ([PR345 Compatibility]: the
+    sharded layout needs each range to split evenly over the ranks)."""
     if tp < 1:
         raise ValueError(f"tp must be >= 1, got {tp}")
     if not sizes:
@@ -102,7 +102,7 @@ def restore_logical(gathered: np.ndarray, sizes: Sequence[int], tp: int) -> np.n
 
 def sharded_projection(x: np.ndarray, w: np.ndarray, sizes: Sequence[int], tp: int) -> np.ndarray:
     """The whole sharded path on one host: every rank's local projection, the rank-major
-    gather, the restore.  Equals linear(x, w) ([PR345 Technical reason]: the gather
-    reconstructs the exact output)."""
+    gather, the restore.  Equals linear(x, w) ([PR345 Technical reason]: gathering the
+    ranks' pieces gives back the replicated result exactly)."""
     parts = [linear(x, merged_column_shard(w, sizes, tp, r)) for r in range(tp)]
     return restore_logical(gather_rank_major(parts), sizes, tp)

@@ -4,7 +4,7 @@ Source: vLLM PR 50656, "[Kimi-K3] Add option to shard the shared expert instead 
 replicating" (Change; Trade-off and why it is opt-in; Evaluation).  Pins: the
 interpolation on functions it must reproduce exactly, a hand-worked collective cost,
 the limits of the decision (free collectives, infinitely slow collectives), and the
-pages' qualitative claim that sharding wins only at low token counts: with a
+pages' qualitative finding that sharding pays off for small token counts only: with a
 weight-bound replicated curve and a shard curve that grows with T, the choice flips
 once, from sharded to replicated.
 """
