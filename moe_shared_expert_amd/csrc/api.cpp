@@ -202,11 +202,15 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   const int64_t fpr = stage == 0 ? 2 : 1;  // weight rows per output feature
   auto tiles_for = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N * fpr + bn - 1) / bn); };
   // Up to two token tiles (M <= 256) the stage is bound by streaming the weights: one
-  // workgroup per compute unit with a 4-stage ring (three K steps in flight), about 224
-  // workgroups: the widest tile (128 x 128, then 128 x 64, then for down 128 x 32) that
-  // reaches 160 workgroups with K split into slices of at least 12 K steps.  Measured
-  // at M = 128 against the rules below: gate_up 58.4 -> 53.1 us (I = 6144),
-  // 18.7 -> 16.4 us (I = 768); down 38.8 -> 33.2 us, 9.7 -> 7.8 us.
+  // workgroup per compute unit with a deep LDS ring, about 224 workgroups.  gate_up takes
+  // 128 x 256 tiles (8 waves, 3 stages) when they reach 160 workgroups with K slices of
+  // at least 12 K steps, else the widest of 128 x 128 (8 waves, 4 stages) and 128 x 64
+  // (4 waves, 4 stages) that does; down the same without the 256-row tile, and 128 x 32
+  // tiles without a K split when K is short (the I of a TP shard) or 128 x 64 tiles
+  // would not reach 160 workgroups.  Measured at M = 64, 128, 256 (graph timings over
+  // distinct weight copies): replicated gate_up 45.6 -> 42.1, 51.9 -> 47.2, 78.4 -> 70.7
+  // us and down 29.0 -> 26.5, 32.9 -> 30.3, 45.2 -> 42.5 us against 4-wave 128 x 128
+  // tiles; TP8 down at M = 256 11.9 -> 10.4 us with 128 x 32 tiles.
   const bool stream_m = !hilo && M <= 256;
   const int64_t ksteps = (K + 63) / 64;
   auto stream_ks = [&](int bn) {
@@ -220,14 +224,20 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (stream_m) {
     gp.bm = 128;
     gp.bn = 64;
-    if (tiles_for(128, 128) * stream_ks(128) >= 160)
+    if (stage == 0 && tiles_for(128, 256) * stream_ks(256) >= 160)
+      gp.bn = 256;
+    else if (tiles_for(128, 128) * stream_ks(128) >= 160)
       gp.bn = 128;
-    else if (stage == 1 && tiles_for(128, 64) * stream_ks(64) < 160)
+    else if (stage == 1 && (K < 2048 || tiles_for(128, 64) * stream_ks(64) < 160))
       gp.bn = 32;
   } else if (!hilo && tiles_for(256, 256) >= 2 * kCUs && K >= 4096) {
     gp.bm = 256;
     gp.bn = 256;
-  } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs)) {
+  } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs) ||
+             (stage == 1 && !hilo && K >= 2048 && tiles_for(128, 128) >= kCUs / 2)) {
+    // The long-K down stage also takes 128 x 128 tiles from half a tile per compute
+    // unit, K split to fill the chip (M = 512, I = 6144: 87.2 -> 72.2 us against
+    // 128 x 64 tiles).
     gp.bm = 128;
     gp.bn = 128;
   } else if (stage == 1 && !hilo && K < 2048 && tiles_for(128, 64) < kCUs) {
@@ -239,6 +249,9 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     gp.bm = 128;
     gp.bn = 64;
   }
+  // Waves: 8 for the 128 x 128 and 256-wide tiles (two waves per SIMD overlap one wave's
+  // LDS reads and barrier with the other's multiplies: M = 2048 down 225 -> 210 us, TP8
+  // gate_up 74.5 -> 71.8 us), 4 for the narrow tiles and the two-plane down tile.
   if (o.wm.load() && o.wn.load()) {
     gp.wm = o.wm.load();
     gp.wn = o.wn.load();
@@ -248,14 +261,20 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (gp.bn <= 64) {
     gp.wm = 4;
     gp.wn = 1;
-  } else {
+  } else if (gp.bn == 256) {
     gp.wm = 2;
+    gp.wn = 4;
+  } else if (hilo) {
+    gp.wm = 2;
+    gp.wn = 2;
+  } else {
+    gp.wm = 4;
     gp.wn = 2;
   }
   if (o.ns.load()) {
     gp.ns = o.ns.load();
   } else if (stream_m) {
-    gp.ns = 4;
+    gp.ns = gp.bn == 256 ? 3 : 4;
   } else {
     // Two stages where compiled (the two-plane 128 x 128 down tile has three).
     gp.ns = 2;

@@ -295,6 +295,35 @@ def test_both_paths_agree_with_oracle(M):
     assert_rms_close(large, ref, BF16_TOL, f"large path M={M}")
 
 
+# Every compiled LDS-tiled configuration (bm, bn, wm, wn, stages), pinned one stage at a
+# time on a shape that spans several tiles with ragged tails in M, N and K.
+GATE_UP_TILES = [(256, 256, 2, 4, 2), (128, 256, 2, 4, 3), (128, 256, 2, 2, 3), (128, 256, 2, 4, 2),
+                 (128, 128, 2, 2, 2), (128, 128, 2, 2, 4), (128, 128, 4, 2, 2), (128, 128, 4, 2, 3),
+                 (128, 128, 4, 2, 4), (256, 128, 4, 2, 2), (256, 128, 4, 2, 3),
+                 (128, 64, 4, 1, 2), (128, 64, 4, 1, 4), (128, 64, 4, 1, 6)]
+DOWN_TILES = GATE_UP_TILES + [(128, 32, 4, 1, 2), (128, 32, 4, 1, 4)]
+
+
+@pytest.mark.parametrize("ksplit", [1, 3])
+@pytest.mark.parametrize("stage,tile", [(0, t) for t in GATE_UP_TILES] + [(1, t) for t in DOWN_TILES])
+def test_every_compiled_tile(stage, tile, ksplit):
+    M, Hh, Ii = 300, 1032, 392
+    x = synth.activations(M, Hh, config=12, copy=1)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=12)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    prev = binding.shared_mlp_set_large_m_threshold(1)
+    try:
+        binding.shared_mlp_tune_gemm(stage, *tile, ksplit=ksplit)
+        p = binding.shared_mlp_plan(M, Hh, Ii, binding.SMLP_BF16, True)
+        assert p["path_name"] == "large_m"
+        assert (p["gate_up_ksplit"] if stage == 0 else p["down_ksplit"]) == ksplit
+        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=True)
+    finally:
+        binding.shared_mlp_tune_gemm(stage)
+        binding.shared_mlp_set_large_m_threshold(prev)
+    assert_rms_close(out, ref, BF16_TOL, f"stage {stage} tile {tile} ksplit {ksplit}")
+
+
 def test_m_zero_leaves_output_untouched():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
     wgu = torch.zeros(2 * 32, 64, dtype=torch.bfloat16, device=DEV)
