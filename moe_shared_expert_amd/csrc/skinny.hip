@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
                                                        int ksplit, int M, int N, void* out,
                                                        int ldo, int out_f32, int h_planes) {
   // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, up to
-  // eight slices in flight at a time, summed in slice order.  Down and projection outputs
+  // sixteen slices in flight at a time, summed in slice order.  Down and projection outputs
   // have row stride ldo (a multiple of 4).
   constexpr int P = GU ? 2 : 1;
   const int N4 = N >> 2;
@@ -508,19 +508,20 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
     const int m = (int)(e / N4), n = (int)(e % N4) * 4;
     const float* base = part + (size_t)m * P * N + n;
     f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-    // Eight slices per batch, all loads of a batch in flight together (the last batch
+    // SB slices per batch, all loads of a batch in flight together (the last batch
     // takes the remaining slices), summed in slice order.
-    for (int s = 0; s < ksplit; s += 8) {
-      f32x4 a[8], b[8];
+    constexpr int SB = 16;
+    for (int s = 0; s < ksplit; s += SB) {
+      f32x4 a[SB], b[SB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < SB; ++q) {
         if (s + q < ksplit) {
           a[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride);
           if (GU) b[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride + N);
         }
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < SB; ++q) {
         if (s + q < ksplit) {
           g += a[q];
           if (GU) u += b[q];
@@ -620,14 +621,17 @@ int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* 
                     int out_f32, int h_planes, hipStream_t s) {
   if (N % 4 != 0 || ldo % 4 != 0) return (int)hipErrorInvalidValue;
   const size_t total = (size_t)M * (N / 4);
-  int blocks = (int)((total + 255) / 256);
-  if (blocks > 2048) blocks = 2048;
+  // Small outputs (a decode step's partials) take 64-thread workgroups so that every
+  // compute unit pulls a share of the partials.
+  const int threads = total >= (size_t)512 * 256 ? 256 : 64;
+  size_t blocks = (total + threads - 1) / threads;
+  if (blocks > (size_t)2048 * 256 / threads) blocks = (size_t)2048 * 256 / threads;
   if (gu)
-    hipLaunchKernelGGL(skinny_finalize<true>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
-                       out, ldo, out_f32, h_planes);
+    hipLaunchKernelGGL(skinny_finalize<true>, dim3((unsigned)blocks), dim3(threads), 0, s, part, ksplit, M,
+                       N, out, ldo, out_f32, h_planes);
   else
-    hipLaunchKernelGGL(skinny_finalize<false>, dim3(blocks), dim3(256), 0, s, part, ksplit, M, N,
-                       out, ldo, out_f32, h_planes);
+    hipLaunchKernelGGL(skinny_finalize<false>, dim3((unsigned)blocks), dim3(threads), 0, s, part, ksplit,
+                       M, N, out, ldo, out_f32, h_planes);
   return (int)hipGetLastError();
 }
 
