@@ -206,42 +206,89 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
     }
   };
 
-  // 32x32x16 fragments: lane l reads tile row (base + l%32), K chunk 2*ks + l/32.  The
-  // fragments of sub-step ks+1 are read while the MFMAs of sub-step ks run.
+  // 32x32x16 fragments: lane l reads tile row (base + l%32), K chunk 2*ks + l/32.
+  // Fragment t of a sub-step: A tiles (plane q, row block i) for t < NA*TM, then B tiles.
   const int fr = lane & 31, fh = lane >> 5;
   const int fsw = chunk_swz(fr);  // row bases are multiples of 32
   constexpr int NFRAG = NA * TM + TN;
-  auto compute = [&](int buf) {
+  constexpr int NMFMA = NA * TM * TN;
+  // One K step.  Wave tiles with at least as many MFMAs as fragment reads per sub-step
+  // (the 256-wide tiles and 128 x 128 on 4 waves) pin the order with scheduling
+  // barriers: the fragments of sub-step 0 are read first, then the hook issues the next
+  // stage's global loads; each sub-step's MFMAs are interleaved with the fragment reads
+  // of the next sub-step, two reads ahead of each MFMA, so every read has most of a
+  // sub-step of MFMAs to land before its use (left to the compiler, the reads drifted
+  // next to their MFMAs and each waited out an LDS round trip: prefill gate_up 1219 ->
+  // 1175 us, down 674 -> 657 us).  Thinner wave tiles, with too few MFMAs to hide the
+  // reads behind, keep the compiler's schedule (measured slightly faster there).
+  constexpr bool PINNED = NMFMA >= NFRAG;
+  auto compute = [&](int buf, auto&& hook) {
     const char* st = lds + buf * STAGE;
     u32x4 fa[2][NA][TM], fb[2][TN];
-    auto read_frags = [&](int slot, int ks) {
+    auto read_frag = [&](int slot, int ks, int t) {
       const int coff = ((2 * ks + fh) ^ fsw) * 16;
-#pragma unroll
-      for (int q = 0; q < NA; ++q)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          fa[slot][q][i] = *reinterpret_cast<const u32x4*>(st + q * A_BYTES + ((wm * TM + i) * 32 + fr) * 128 + coff);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
+      if (t < NA * TM) {
+        const int q = t / TM, i = t % TM;
+        fa[slot][q][i] = *reinterpret_cast<const u32x4*>(st + q * A_BYTES + ((wm * TM + i) * 32 + fr) * 128 + coff);
+      } else {
+        const int j = t - NA * TM;
         fb[slot][j] = *reinterpret_cast<const u32x4*>(st + NA * A_BYTES + ((wn * TN + j) * 32 + fr) * 128 + coff);
+      }
     };
-    read_frags(0, 0);
+    if constexpr (!PINNED) {
+      hook();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cur = ks & 1;
-      if (ks < 3) read_frags(cur ^ 1, ks + 1);
+      for (int t = 0; t < NFRAG; ++t) read_frag(0, 0, t);
 #pragma unroll
-      for (int q = 0; q < NA; ++q)
+      for (int ks = 0; ks < 4; ++ks) {
+        const int cur = ks & 1;
+        if (ks < 3) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+          for (int t = 0; t < NFRAG; ++t) read_frag(cur ^ 1, ks + 1, t);
+        }
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[cur][q][i], fb[cur][j], acc[i][j]);
-      if (ks < 3) {
-        // Interleave: one fragment read, then a share of the MFMAs.
+        for (int q = 0; q < NA; ++q)
 #pragma unroll
-        for (int t = 0; t < NFRAG; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, NA * TM * TN / NFRAG, 0);  // MFMA
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[cur][q][i], fb[cur][j], acc[i][j]);
+        if (ks < 3) {
+          // Interleave: one fragment read, then a share of the MFMAs.
+#pragma unroll
+          for (int t = 0; t < NFRAG; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, NA * TM * TN / NFRAG, 0);  // MFMA
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NFRAG; ++t) read_frag(0, 0, t);
+      __builtin_amdgcn_sched_barrier(0);
+      hook();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int cur = ks & 1;
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int m = (q * TM + i) * TN + j;
+              if (ks < 3) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+                  if (2 * m + r < NFRAG) read_frag(cur ^ 1, ks + 1, 2 * m + r);
+              }
+              acc[i][j] = mfma32x32x16(fa[cur][q][i], fb[cur][j], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        if (ks < 3) {
+#pragma unroll
+          for (int t = 2 * NMFMA; t < NFRAG; ++t) read_frag(cur ^ 1, ks + 1, t);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -257,8 +304,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
     // that the next loads overwrite (it held step kt-1).
     wait_steps<LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
     block_barrier();
-    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
-    compute(kt % NS);
+    compute(kt % NS, [&] {
+      if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
+    });
   }
 
   // Epilogue.  32x32 output: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
