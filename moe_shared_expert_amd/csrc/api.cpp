@@ -313,6 +313,38 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   return true;
 }
 
+// The 256 x 256 down tile runs one workgroup per compute unit; when its tiles fill the
+// chip a whole number of times plus a last round that is at most 60% full (M = 8192,
+// H = 7168: 896 tiles = 3.5 rounds), the columns of the whole rounds keep that tile and
+// the remaining columns run as a second launch of 128 x 128 tiles (8 waves, two
+// workgroups per compute unit), which fills the chip in one round instead of leaving
+// half of it idle.  Not applied to a pinned down tile.
+void split_down_tail(int64_t M, int64_t H, int64_t I, smlp::Plan* p) {
+  smlp::GemmPlan& g = p->gdn;
+  if (g_gtune[1].bm.load() || g.bm != 256 || g.bn != 256 || g.ksplit != 1) return;
+  const int64_t rounds = g.tiles / kCUs, rem = g.tiles % kCUs;
+  if (rounds < 1 || rem == 0 || rem * 10 > kCUs * 6) return;
+  const int64_t cols = rounds * kCUs / g.tiles_m;  // 256-wide column tiles in whole rounds
+  const int64_t tiles_n = (H + 255) / 256;
+  if (cols < 1 || cols >= tiles_n) return;
+  smlp::GemmPlan t{};
+  t.bm = 128;
+  t.bn = 128;
+  t.wm = 4;
+  t.wn = 2;
+  t.ns = 2;
+  if (!smlp::gemm_instantiated(1, false, t.bm, t.bn, t.wm, t.wn, t.ns)) return;
+  const int64_t rest = H - cols * 256;
+  t.tiles_m = (int)((M + 127) / 128);
+  t.tiles = (int)(t.tiles_m * ((rest + 127) / 128));
+  t.ksplit = 1;
+  t.kslice = (int)((I + 63) / 64 * 64);
+  g.tiles = (int)(g.tiles_m * cols);
+  p->gdn_tail = t;
+  p->dn_split = cols * 256;
+  p->kernels += 1;
+}
+
 int out_elem(int dtype, int partial_fp32) { return (dtype == SMLP_FP32 || partial_fp32) ? 4 : 2; }
 
 // Shape/dtype validation and plan; no pointer checks.
@@ -386,6 +418,7 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     }
     p->part_bytes = round_up(part, 256);
     p->kernels = 2 + (p->ggu.ksplit > 1) + (p->gdn.ksplit > 1);
+    split_down_tail(M, H, I, p);
   }
   p->h_offset = 0;
   p->part_offset = p->h_bytes;
@@ -605,7 +638,7 @@ int shared_mlp_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32
     plan->gate_up_ksplit = p.ggu.ksplit;
     plan->down_ksplit = p.gdn.ksplit;
     plan->gate_up_blocks = p.ggu.tiles * p.ggu.ksplit;
-    plan->down_blocks = p.gdn.tiles * p.gdn.ksplit;
+    plan->down_blocks = p.gdn.tiles * p.gdn.ksplit + (p.dn_split ? p.gdn_tail.tiles : 0);
   } else {
     plan->gate_up_ksplit = plan->down_ksplit = 1;
     plan->gate_up_blocks = plan->down_blocks = 0;

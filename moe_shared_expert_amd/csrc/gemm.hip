@@ -443,6 +443,24 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = p.partial_fp32 ? 1 : 0;
   a.h_planes = 1;
+  if (p.dn_split) {
+    // Columns [0, dn_split) with the main tile, then the rest with the tail tile: each
+    // launch sees its own weight rows and output columns (row stride H).
+    a.N = (int)p.dn_split;
+    a.b_rows = a.N;
+    a.ldo = (int)p.H;
+    int rc = launch_mode<GM_DOWN_BF16>(p.gdn, a, s);
+    if (rc) return rc;
+    GArgs t = a;
+    t.b = a.b + (size_t)p.dn_split * p.ldwd;
+    t.N = (int)(p.H - p.dn_split);
+    t.b_rows = t.N;
+    t.tiles_m = p.gdn_tail.tiles_m;
+    t.tiles_n = p.gdn_tail.tiles / p.gdn_tail.tiles_m;
+    t.kslice = p.gdn_tail.kslice;
+    t.out = static_cast<char*>(out) + (size_t)p.dn_split * (a.out_f32 ? 4 : 2);
+    return launch_mode<GM_DOWN_BF16>(p.gdn_tail, t, s);
+  }
   int rc = p.h_dtype == SMLP_BF16_HILO ? launch_mode<GM_DOWN_HILO>(p.gdn, a, s)
                                       : launch_mode<GM_DOWN_BF16>(p.gdn, a, s);
   if (rc || p.gdn.ksplit == 1) return rc;

@@ -232,6 +232,21 @@ def test_prefill_m8192_sampled_rows(full_layer):
     assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, "prefill M=8192 sampled")
 
 
+@pytest.mark.parametrize("partial", [False, True])
+def test_down_column_split_ragged(partial):
+    # 256 x 256 down tiles that fill the chip twice plus a small last round: the whole
+    # rounds' columns keep that tile, the ragged remaining columns run as a second launch.
+    M, Hh, Ii = 8100, 4360, 4096
+    p = binding.shared_mlp_plan(M, Hh, Ii, binding.SMLP_BF16, partial)
+    assert p["path_name"] == "large_m" and p["kernels"] == 3, p
+    x = synth.activations(M, Hh, config=13)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=13)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=partial)
+    rows = np.array([0, 1, 127, 128, 4095, 4096, 8063, 8064, 8099])
+    ref = oracle.swiglu_mlp(f64(x[rows]), f64(wgu), f64(wd))
+    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"column split partial={partial}")
+
+
 # ---------------------------------------------- M sweep, replicated and TP8 shard
 @pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 2048])
 def test_sweep_replicated(M, full_layer):
