@@ -205,12 +205,15 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   // workgroup per compute unit with a deep LDS ring, about 224 workgroups.  gate_up takes
   // 128 x 256 tiles (8 waves, 3 stages) when they reach 160 workgroups with K slices of
   // at least 12 K steps, else the widest of 128 x 128 (8 waves, 4 stages) and 128 x 64
-  // (4 waves, 4 stages) that does; down the same without the 256-row tile, and 128 x 32
-  // tiles without a K split when K is short (the I of a TP shard) or 128 x 64 tiles
-  // would not reach 160 workgroups.  Measured at M = 64, 128, 256 (graph timings over
-  // distinct weight copies): replicated gate_up 45.6 -> 42.1, 51.9 -> 47.2, 78.4 -> 70.7
-  // us and down 29.0 -> 26.5, 32.9 -> 30.3, 45.2 -> 42.5 us against 4-wave 128 x 128
-  // tiles; TP8 down at M = 256 11.9 -> 10.4 us with 128 x 32 tiles.
+  // (4 waves, 4 stages) that does; down the same without the 256-row tile; a short-K
+  // down (the I of a TP shard) takes 64 x 64 tiles on a 2 x 2 wave grid without a K
+  // split (each workgroup reads half the tokens' h instead of all of it), and a down
+  // whose 128 x 64 tiles would not reach 160 workgroups 128 x 32 tiles.  Measured at
+  // M = 64, 128, 256 (graph timings over distinct weight copies): replicated gate_up
+  // 45.6 -> 42.1, 51.9 -> 47.2, 78.4 -> 70.7 us and down 29.0 -> 26.5, 32.9 -> 30.3,
+  // 45.2 -> 42.5 us against 4-wave 128 x 128 tiles; TP8 down 7.45 -> 7.21, 7.82 -> 7.51,
+  // 11.9 -> 9.31 us and TP16 down 5.49 -> 5.34, 5.84 -> 5.64, 7.55 -> 7.02 us against
+  // 128 x 32 / 128 x 64 tiles.
   const bool stream_m = !hilo && M <= 256;
   const int64_t ksteps = (K + 63) / 64;
   auto stream_ks = [&](int bn) {
@@ -224,12 +227,16 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (stream_m) {
     gp.bm = 128;
     gp.bn = 64;
-    if (stage == 0 && tiles_for(128, 256) * stream_ks(256) >= 160)
+    if (stage == 0 && tiles_for(128, 256) * stream_ks(256) >= 160) {
       gp.bn = 256;
-    else if (tiles_for(128, 128) * stream_ks(128) >= 160)
+    } else if (tiles_for(128, 128) * stream_ks(128) >= 160) {
       gp.bn = 128;
-    else if (stage == 1 && (K < 2048 || tiles_for(128, 64) * stream_ks(64) < 160))
+    } else if (stage == 1 && K < 2048) {
+      gp.bm = 64;
+      gp.bn = 64;
+    } else if (stage == 1 && tiles_for(128, 64) * stream_ks(64) < 160) {
       gp.bn = 32;
+    }
   } else if (!hilo && tiles_for(256, 256) >= 2 * kCUs && K >= 4096) {
     gp.bm = 256;
     gp.bn = 256;
@@ -258,6 +265,9 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (gp.bm == 256) {
     gp.wm = 2;
     gp.wn = 4;
+  } else if (gp.bm == 64) {
+    gp.wm = 2;
+    gp.wn = 2;
   } else if (gp.bn <= 64) {
     gp.wm = 4;
     gp.wn = 1;
@@ -285,7 +295,9 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   const int64_t tiles = tiles_for(gp.bm, gp.bn);
   gp.tiles = (int)tiles;
   int64_t ks = o.ksplit.load();
-  if (!ks && stream_m && gp.bm == 128) {
+  if (!ks && stream_m && gp.bm == 64) {
+    ks = 1;
+  } else if (!ks && stream_m && gp.bm == 128) {
     ks = gp.bn == 32 ? 1 : stream_ks(gp.bn);
   } else if (!ks) {
     if (gp.bn == 32) {
@@ -848,7 +860,7 @@ int shared_mlp_tune_h_planes(int planes) {
 }
 
 int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int ksplit) {
-  if (stage < 0 || stage > 2 || !(bm == 0 || bm == 128 || bm == 256) ||
+  if (stage < 0 || stage > 2 || !(bm == 0 || bm == 64 || bm == 128 || bm == 256) ||
       !(bn == 0 || bn == 32 || bn == 64 || bn == 128 || bn == 256) || (bm == 0) != (bn == 0) ||
       !(wm == 0 || wm == 1 || wm == 2 || wm == 4) || !(wn == 0 || wn == 1 || wn == 2 || wn == 4) ||
       (wm == 0) != (wn == 0) || ns < 0 || ns > 8 || ksplit < 0 || ksplit > 1024)

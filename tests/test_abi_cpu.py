@@ -88,7 +88,17 @@ def test_default_threshold_and_gemm_tuning(L):
     # prefill: 256 x 256 tiles, one per workgroup, no K split
     p = binding.shared_mlp_plan(8192, H, I)
     assert p["gate_up_blocks"] == (8192 // 256) * (2 * I // 256) and p["gate_up_ksplit"] == 1
-    assert p["down_blocks"] == (8192 // 256) * (H // 256) and p["down_ksplit"] == 1
+    # down: 256 x 256 tiles for the columns of three whole rounds over 256 CUs (768 tiles),
+    # the last 1024 columns as one round of 128 x 128 tiles (512), a third launch
+    assert p["down_blocks"] == 3 * 256 + (8192 // 128) * ((H - 3 * 256 * 256 // (8192 // 256)) // 128)
+    assert p["down_ksplit"] == 1 and p["kernels"] == 3
+    # a pinned down tile is never split
+    binding.shared_mlp_tune_gemm(1, bm=256, bn=256, wm=2, wn=4, ns=2)
+    try:
+        p = binding.shared_mlp_plan(8192, H, I)
+        assert p["down_blocks"] == (8192 // 256) * (H // 256) and p["kernels"] == 2
+    finally:
+        binding.shared_mlp_tune_gemm(1)
     try:
         binding.shared_mlp_tune_gemm(0, bm=128, bn=128, wm=2, wn=2, ns=4, ksplit=2)
         p = binding.shared_mlp_plan(512, H, I)
