@@ -445,7 +445,10 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
   a.h_planes = 1;
   if (p.dn_split) {
     // Columns [0, dn_split) with the main tile, then the rest with the tail tile: each
-    // launch sees its own weight rows and output columns (row stride H).
+    // launch sees its own weight rows and output columns (row stride H).  Planned for
+    // one plane of h only.
+    if (p.h_dtype == SMLP_BF16_HILO || p.gdn.ksplit != 1 || p.gdn_tail.ksplit != 1)
+      return (int)hipErrorInvalidConfiguration;
     a.N = (int)p.dn_split;
     a.b_rows = a.N;
     a.ldo = (int)p.H;
