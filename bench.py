@@ -504,7 +504,10 @@ def sweep(dev):
             alg = roofline.algorithmic_bytes(M, H, I_r, 2, 4 if partial else 2)
             fl = roofline.flops(M, H, I_r)
             pts.append((M, us))
+            bound, t_roof = roofline.roofline_us(M, H, I_r, 4 if partial else 2)
             print(json.dumps({"sweep": layout, "M": M, "I_r": I_r, "us_per_layer": round(us, 2),
+                              "bound": bound, "roofline_us": round(t_roof, 2),
+                              "roofline_frac": round(t_roof / us, 4),
                               "gbs": round(alg / us / 1e3, 1),
                               "hbm_frac": round(alg / us / 1e3 / roofline.HBM_PEAK_GBS, 4),
                               "tflops": round(fl / us / 1e6, 1),

@@ -44,3 +44,11 @@ def latent_projection_bytes(m: int, k: int, n_r: int, elem: int = 2, out_elem: i
 def latent_restore_bytes(m: int, n: int, elem: int = 2) -> int:
     """The gathered output read once and the logical output written once."""
     return 2 * m * n * elem
+
+
+def roofline_us(m: int, hidden: int, inter: int, out_elem: int = 2):
+    """(bound, microseconds) of one layer at the peaks: the larger of the algorithmic
+    bytes at HBM_PEAK_GBS and the flops at BF16_MFMA_PEAK_TFLOPS."""
+    t_hbm = algorithmic_bytes(m, hidden, inter, 2, out_elem) / (HBM_PEAK_GBS * 1e3)
+    t_mfma = flops(m, hidden, inter) / (BF16_MFMA_PEAK_TFLOPS * 1e6)
+    return ("hbm", t_hbm) if t_hbm >= t_mfma else ("mfma", t_mfma)

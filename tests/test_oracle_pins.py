@@ -298,6 +298,23 @@ def test_printed_byte_counts_pin_the_accounting():
         assert round(b / units[unit], 1) == float(printed), name
 
 
+def test_roofline_bound_and_ridge():
+    """The per-layer roofline: HBM-bound while 6*M*H*I flops at 2.5 PFLOP/s take less
+    than the algorithmic bytes at 8 TB/s.  Hand-worked: replicated decode M = 16 moves
+    3*7168*6144*2 + 2*16*7168*2 bytes = 264,699,904 B -> 33.087 us; prefill M = 8192
+    does 6*8192*7168*6144 = 2.1646e12 flops -> 865.9 us.  The replicated ridge in M
+    (3*M*I / (3*I + 2*M) = 312.5 flop/B at 2.5e15 / 8e12) lies between 256 and 512."""
+    b, t = roofline.roofline_us(16, 7168, 6144)
+    assert b == "hbm" and abs(t - 264699904 / 8e6) < 1e-9
+    b, t = roofline.roofline_us(8192, 7168, 6144)
+    assert b == "mfma" and abs(t - 6 * 8192 * 7168 * 6144 / 2.5e9) < 1e-6
+    assert roofline.roofline_us(256, 7168, 6144)[0] == "hbm"
+    assert roofline.roofline_us(512, 7168, 6144)[0] == "mfma"
+    # a TP8 rank's fp32 partial (4-byte output) stays HBM-bound through M = 512
+    assert roofline.roofline_us(512, 7168, 768, 4)[0] == "hbm"
+    assert roofline.roofline_us(2048, 7168, 768, 4)[0] == "mfma"
+
+
 def test_statistical_output_scale():
     """x ~ N(0,1), W ~ N(0, 1/fan_in) gives RMS(out) ~ sqrt(E[silu(g)^2] * I_r / I)
     with g ~ N(0,1); E[silu^2] by quadrature.  Pins the generator's std and
