@@ -186,14 +186,15 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
   return true;
 }
 
-// LDS-tiled GEMM stage plan (measured on MI355X over M = 64 .. 8192, I = 768 and 6144):
-// 256 x 256 tiles (8 waves, 128 x 64 per wave) when they fill the chip at least twice
-// over and K is long; otherwise 128 x 128 tiles (4 waves) when they fill the chip
-// (gate_up) or fill it twice (down); down with a short K and few tiles: 128 x 32 tiles
-// without a K split; else 128 x 64 tiles with a K split.
-// Two LDS stages, so that two workgroups share a compute unit, and a K split over
-// workgroups when the tiles alone leave compute units idle.  N counts gate_up features
-// (two weight rows each) or down rows.  Returns false if a pinned tile is not compiled.
+// LDS-tiled GEMM stage plan (measured on MI355X over M = 64 .. 8192, I = 384, 768 and
+// 6144).  M > 256: 256 x 256 tiles (8 waves, 128 x 64 per wave) when they fill the chip
+// at least twice over and K is long; otherwise 128 x 128 tiles (8 waves) when they fill
+// the chip (gate_up) or fill it twice (down), or for a long-K down from half a tile per
+// compute unit; down with a short K and few tiles: 128 x 32 tiles without a K split;
+// else 128 x 64 tiles with a K split.  Two LDS stages, so that two workgroups share a
+// compute unit, and a K split over workgroups when the tiles alone leave compute units
+// idle.  M <= 256: the weight-streaming rules below.  N counts gate_up features (two
+// weight rows each) or down rows.  Returns false if a pinned tile is not compiled.
 // `ov` replaces the stage's tuning overrides (the plain projection plans as down).
 bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::GemmPlan* out,
                const GemmOverride* ov = nullptr) {
