@@ -222,6 +222,10 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     if (ks > ksteps / 12) ks = ksteps / 12;
     return ks < 1 ? (int64_t)1 : ks;
   };
+  // 256-token tiles only where M fills at least 3/4 of them (gate_up: 85%; M = 400 was
+  // 113 -> 117 us on 256 x 128 tiles, 78% full, while its down stage gained 63.5 -> 61.5).
+  const int64_t padded256 = (M + 255) / 256 * 256;
+  const bool full256 = stage == 0 ? M * 20 >= 17 * padded256 : M * 4 >= 3 * padded256;
   if (o.bm.load() && o.bn.load()) {
     gp.bm = o.bm.load();
     gp.bn = o.bn.load();
@@ -241,6 +245,19 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!hilo && tiles_for(256, 256) >= 2 * kCUs && K >= 4096) {
     gp.bm = 256;
     gp.bn = 256;
+  } else if (!hilo && stage == 0 && K >= 4096 && full256 && tiles_for(256, 256) >= kCUs &&
+             tiles_for(256, 256) * 10 >= 7 * kCUs * ((tiles_for(256, 256) + kCUs - 1) / kCUs)) {
+    // gate_up whose 256 x 256 tiles fill the chip once with rounds at least 70% full
+    // (M = 2048, I = 6144: 384 tiles, 376 -> 356 us against 128 x 128 tiles).
+    gp.bm = 256;
+    gp.bn = 256;
+  } else if (!hilo && K >= 4096 && M <= 1024 && full256 &&
+             (stage == 0 ? tiles_for(256, 128) >= kCUs / 2 : tiles_for(128, 128) < kCUs)) {
+    // Medium M, long K: 256 x 128 tiles (8 waves, 3 stages) with a K split to about three
+    // workgroups per compute unit (gate_up) or two slices (down).  M = 512: gate_up
+    // 131.7 -> 122.0 us, down 73.0 -> 63.0 us; M = 1024: gate_up 237 -> 207 us.
+    gp.bm = 256;
+    gp.bn = 128;
   } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs) ||
              (stage == 1 && !hilo && K >= 2048 && tiles_for(128, 128) >= kCUs / 2)) {
     // The long-K down stage also takes 128 x 128 tiles from half a tile per compute
@@ -263,6 +280,9 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   if (o.wm.load() && o.wn.load()) {
     gp.wm = o.wm.load();
     gp.wn = o.wn.load();
+  } else if (gp.bm == 256 && gp.bn == 128) {
+    gp.wm = 4;
+    gp.wn = 2;
   } else if (gp.bm == 256) {
     gp.wm = 2;
     gp.wn = 4;
@@ -286,6 +306,8 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     gp.ns = o.ns.load();
   } else if (stream_m) {
     gp.ns = gp.bn == 256 ? 3 : 4;
+  } else if (gp.bm == 256 && gp.bn == 128) {
+    gp.ns = 3;
   } else {
     // Two stages where compiled (the two-plane 128 x 128 down tile has three).
     gp.ns = 2;
@@ -301,7 +323,10 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!ks && stream_m && gp.bm == 128) {
     ks = gp.bn == 32 ? 1 : stream_ks(gp.bn);
   } else if (!ks) {
-    if (gp.bn == 32) {
+    if (gp.bm == 256 && gp.bn == 128) {
+      ks = stage == 0 ? (3 * kCUs + tiles - 1) / tiles : 2;
+      if (ks > 4) ks = 4;
+    } else if (gp.bn == 32) {
       ks = 1;
     } else if (gp.bn == 64 && gp.bm == 128) {
       // Few weight tiles (medium M): split K until about 3 (gate_up) or 1.75 (down)
