@@ -351,36 +351,41 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   return true;
 }
 
-// The 256 x 256 down tile runs one workgroup per compute unit; when its tiles fill the
-// chip a whole number of times plus a last round that is at most 60% full (M = 8192,
-// H = 7168: 896 tiles = 3.5 rounds), the columns of the whole rounds keep that tile and
-// the remaining columns run as a second launch of 128 x 128 tiles (8 waves, two
-// workgroups per compute unit), which fills the chip in one round instead of leaving
-// half of it idle.  Not applied to a pinned down tile.
-void split_down_tail(int64_t M, int64_t H, int64_t I, smlp::Plan* p) {
-  smlp::GemmPlan& g = p->gdn;
-  if (g_gtune[1].bm.load() || g.bm != 256 || g.bn != 256 || g.ksplit != 1) return;
-  const int64_t rounds = g.tiles / kCUs, rem = g.tiles % kCUs;
-  if (rounds < 1 || rem == 0 || rem * 10 > kCUs * 6) return;
-  const int64_t cols = rounds * kCUs / g.tiles_m;  // 256-wide column tiles in whole rounds
-  const int64_t tiles_n = (H + 255) / 256;
-  if (cols < 1 || cols >= tiles_n) return;
+// A 256 x 256 plan runs one workgroup per compute unit; when its tiles fill the chip a
+// whole number of times plus a partial last round (M = 8192, H = 7168 down: 896 tiles =
+// 3.5 rounds; M = 2048, I = 6144 gate_up: 384 tiles = 1.5 rounds), the output columns of
+// the whole rounds keep that tile and the remaining
+// columns (down rows or gate_up features) run as a second launch of 128 x 128 tiles
+// (8 waves, two workgroups per compute unit), which fills the chip in one round instead
+// of leaving part of it idle.  Not applied to a pinned tile.  N counts down rows or
+// gate_up features; returns whether the plan was split.
+bool split_columns(int stage, int64_t M, int64_t N, int64_t K, smlp::GemmPlan* g, smlp::GemmPlan* tail,
+                   int64_t* split) {
+  if (g_gtune[stage].bm.load() || g->bm != 256 || g->bn != 256 || g->ksplit != 1) return false;
+  // Split only where at least 1/8 of the unsplit plan's round slots would sit idle
+  // (gate_up at M = 6144, 4.5 rounds: 930.7 -> 948.8 us split, against 2048: 359.7 ->
+  // 328.9 and 3072: 533.7 -> 488.2 us).
+  const int64_t rounds = g->tiles / kCUs, slots = (g->tiles + kCUs - 1) / kCUs * kCUs;
+  if (rounds < 1 || g->tiles % kCUs == 0 || (slots - g->tiles) * 8 < slots) return false;
+  const int64_t width = stage == 0 ? 128 : 256;  // output columns per 256 x 256 tile
+  const int64_t cols = rounds * kCUs / g->tiles_m;  // column tiles in whole rounds
+  if (cols < 1 || cols >= (N + width - 1) / width) return false;
   smlp::GemmPlan t{};
   t.bm = 128;
   t.bn = 128;
   t.wm = 4;
   t.wn = 2;
   t.ns = 2;
-  if (!smlp::gemm_instantiated(1, false, t.bm, t.bn, t.wm, t.wn, t.ns)) return;
-  const int64_t rest = H - cols * 256;
+  if (!smlp::gemm_instantiated(stage, false, t.bm, t.bn, t.wm, t.wn, t.ns)) return false;
+  const int64_t rest = N - cols * width, twidth = width / 2;
   t.tiles_m = (int)((M + 127) / 128);
-  t.tiles = (int)(t.tiles_m * ((rest + 127) / 128));
+  t.tiles = (int)(t.tiles_m * ((rest + twidth - 1) / twidth));
   t.ksplit = 1;
-  t.kslice = (int)((I + 63) / 64 * 64);
-  g.tiles = (int)(g.tiles_m * cols);
-  p->gdn_tail = t;
-  p->dn_split = cols * 256;
-  p->kernels += 1;
+  t.kslice = (int)((K + 63) / 64 * 64);
+  g->tiles = (int)(g->tiles_m * cols);
+  *tail = t;
+  *split = cols * width;
+  return true;
 }
 
 int out_elem(int dtype, int partial_fp32) { return (dtype == SMLP_FP32 || partial_fp32) ? 4 : 2; }
@@ -456,7 +461,8 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     }
     p->part_bytes = round_up(part, 256);
     p->kernels = 2 + (p->ggu.ksplit > 1) + (p->gdn.ksplit > 1);
-    split_down_tail(M, H, I, p);
+    if (split_columns(1, M, H, I, &p->gdn, &p->gdn_tail, &p->dn_split)) p->kernels += 1;
+    if (!hilo && split_columns(0, M, I, H, &p->ggu, &p->ggu_tail, &p->gu_split)) p->kernels += 1;
   }
   p->h_offset = 0;
   p->part_offset = p->h_bytes;
@@ -675,7 +681,7 @@ int shared_mlp_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32
   } else if (p.path == SMLP_PATH_LARGE_M) {
     plan->gate_up_ksplit = p.ggu.ksplit;
     plan->down_ksplit = p.gdn.ksplit;
-    plan->gate_up_blocks = p.ggu.tiles * p.ggu.ksplit;
+    plan->gate_up_blocks = p.ggu.tiles * p.ggu.ksplit + (p.gu_split ? p.ggu_tail.tiles : 0);
     plan->down_blocks = p.gdn.tiles * p.gdn.ksplit + (p.dn_split ? p.gdn_tail.tiles : 0);
   } else {
     plan->gate_up_ksplit = plan->down_ksplit = 1;

@@ -54,17 +54,18 @@ struct GArgs {
   float* part;            // gridDim.y > 1: fp32 partial sums [slices][M][P*N]
   int out_f32;
   int h_planes;           // gate_up: planes of h to store (1 or 2)
+  int ldh;                // gate_up: elements between rows of h (>= N; planes are M * ldh apart)
 };
 
 constexpr int BK = 64;      // K elements per step (128 bytes of a row)
 constexpr int GROUP_M = 8;  // token tiles per group in the tile order
 constexpr int XCDS = 8;
 
-__device__ __forceinline__ void put_h(void* base, int M, int N, int m, int n, float h, int planes) {
+__device__ __forceinline__ void put_h(void* base, int M, int ld, int m, int n, float h, int planes) {
   const uint32_t hi = f2bf(h);
   uint16_t* p = reinterpret_cast<uint16_t*>(base);
-  p[(size_t)m * N + n] = (uint16_t)hi;
-  if (planes == 2) p[(size_t)M * N + (size_t)m * N + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
+  p[(size_t)m * ld + n] = (uint16_t)hi;
+  if (planes == 2) p[(size_t)M * ld + (size_t)m * ld + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
 }
 
 // Swizzle of the 16-byte chunks within tile row r.
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
             row[f] = gate;
             row[g.N + f] = up;
           } else {
-            put_h(g.out, g.M, g.N, m, f, silu_mul(gate, up), g.h_planes);
+            put_h(g.out, g.M, g.ldh, m, f, silu_mul(gate, up), g.h_planes);
           }
         }
       } else {
@@ -418,6 +419,24 @@ int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, voi
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = 0;
   a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
+  a.ldh = a.N;
+  if (p.gu_split) {
+    // Features [0, gu_split) with the main tile, then the rest with the tail tile: each
+    // launch sees its own gate rows (its up rows up_off further on) and h columns.
+    if (a.h_planes != 1 || p.ggu.ksplit != 1 || p.ggu_tail.ksplit != 1) return (int)hipErrorInvalidConfiguration;
+    a.N = (int)p.gu_split;
+    int rc = launch_mode<GM_GATE_UP>(p.ggu, a, s);
+    if (rc) return rc;
+    GArgs t = a;
+    t.b = a.b + (size_t)p.gu_split * a.ldb;
+    t.N = (int)(p.I - p.gu_split);
+    t.b_rows = t.up_off + t.N;
+    t.tiles_m = p.ggu_tail.tiles_m;
+    t.tiles_n = p.ggu_tail.tiles / p.ggu_tail.tiles_m;
+    t.kslice = p.ggu_tail.kslice;
+    t.out = static_cast<char*>(a.out) + (size_t)p.gu_split * 2;
+    return launch_mode<GM_GATE_UP>(p.ggu_tail, t, s);
+  }
   int rc = launch_mode<GM_GATE_UP>(p.ggu, a, s);
   if (rc || p.ggu.ksplit == 1) return rc;
   return launch_finalize(true, a.part, p.ggu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);

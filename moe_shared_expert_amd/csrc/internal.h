@@ -46,10 +46,10 @@ struct Plan {
   size_t workspace_bytes;
   SkinnyPlan gu, dn;
   GemmPlan ggu, gdn;
-  // Large-M down stage split by output columns: gdn covers columns [0, dn_split) in whole
-  // rounds of workgroups and gdn_tail the rest (dn_split = 0: no split).
-  GemmPlan gdn_tail;
-  int64_t dn_split;
+  // Large-M stages split by output columns: ggu / gdn cover features / rows [0, split)
+  // in whole rounds of workgroups and the tail plan the rest (split = 0: no split).
+  GemmPlan ggu_tail, gdn_tail;
+  int64_t gu_split, dn_split;
   int kernels;
   // Weight views (a rank's slice read in place from full weights): rows between a gate
   // row and its up row in w_gate_up (I for whole weights), and the row stride of w_down

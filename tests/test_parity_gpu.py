@@ -247,6 +247,22 @@ def test_down_column_split_ragged(partial):
     assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"column split partial={partial}")
 
 
+def test_gate_up_column_split_ragged():
+    # gate_up 256 x 256 tiles that fill the chip once plus a half-full round: the features
+    # of the whole round keep that tile, the ragged remaining features run as a second
+    # launch that writes its columns of h in place.
+    M, Hh, Ii = 2000, 7168, 6104
+    p = binding.shared_mlp_plan(M, Hh, Ii)
+    assert p["path_name"] == "large_m" and p["kernels"] == 3, p
+    assert p["gate_up_blocks"] == 8 * 32 + 16 * ((Ii - 32 * 128 + 63) // 64), p
+    x = synth.activations(M, Hh, config=14)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=14)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
+    rows = np.array([0, 1, 127, 128, 255, 256, 1023, 1791, 1792, 1999])
+    ref = oracle.swiglu_mlp(f64(x[rows]), f64(wgu), f64(wd))
+    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, "gate_up column split")
+
+
 # ---------------------------------------------- M sweep, replicated and TP8 shard
 @pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 2048])
 def test_sweep_replicated(M, full_layer):
