@@ -236,9 +236,12 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
       gp.bn = 256;
     } else if (tiles_for(128, 128) * stream_ks(128) >= 160) {
       gp.bn = 128;
-    } else if (stage == 1 && K < 2048) {
+    } else if (stage == 1 && K < 2048 && M <= 128) {
       gp.bm = 64;
       gp.bn = 64;
+    } else if (stage == 1 && K < 2048) {
+      gp.wm = 4;  // two token tiles: 128 x 64 on 8 waves without a K split
+      gp.wn = 2;
     } else if (stage == 1 && tiles_for(128, 64) * stream_ks(64) < 160) {
       gp.bn = 32;
     }
@@ -280,6 +283,13 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   if (o.wm.load() && o.wn.load()) {
     gp.wm = o.wm.load();
     gp.wn = o.wn.load();
+  } else if (gp.wm && gp.wn) {
+    // set with the tile above
+  } else if (stream_m && stage == 0 && gp.bm == 128 && gp.bn == 64) {
+    // 8 waves, each with one 32-column MFMA tile of 16 gate and 16 up columns (TP8 gate_up
+    // at M = 64 / 128: 14.1 -> 13.2, 16.0 -> 15.6 us; TP16 13.6 -> 12.5, 14.5 -> 14.0 us)
+    gp.wm = 4;
+    gp.wn = 2;
   } else if (gp.bm == 256 && gp.bn == 128) {
     gp.wm = 4;
     gp.wn = 2;
@@ -318,7 +328,7 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   const int64_t tiles = tiles_for(gp.bm, gp.bn);
   gp.tiles = (int)tiles;
   int64_t ks = o.ksplit.load();
-  if (!ks && stream_m && gp.bm == 64) {
+  if (!ks && stream_m && (gp.bm == 64 || (stage == 1 && K < 2048))) {
     ks = 1;
   } else if (!ks && stream_m && gp.bm == 128) {
     ks = gp.bn == 32 ? 1 : stream_ks(gp.bn);

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
   constexpr int AL = BM / 8 / W, BL = BN / 8 / W;      // 1 KB block loads per wave per step
   static_assert(AL * W * 8 == BM && BL * W * 8 == BN, "tile / wave mismatch");
-  static_assert(!GU || TN % 2 == 0, "gate_up pairs gate and up MFMA tiles");
+  static_assert(!GU || TN % 2 == 0 || TN == 1, "gate_up pairs gate and up MFMA tiles or columns");
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int STAGE = NA * A_BYTES + B_BYTES;
   constexpr int LPS = NA * AL + BL;  // load instructions per wave per step
@@ -311,7 +311,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   }
 
   // Epilogue.  32x32 output: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
-  // gate_up: MFMA tile j holds gate features and tile j + TN/2 the matching up rows.
+  // gate_up: MFMA tile j holds gate features and tile j + TN/2 the matching up rows; with
+  // one MFMA tile column per wave (TN = 1) its columns 0-15 are gate features and 16-31
+  // the matching up rows, brought together by exchanging lanes l and l ^ 16.
   const bool split = gridDim.y > 1;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -320,6 +322,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
       // One output row at a time keeps the accumulators from all moving to VGPRs at once.
       __builtin_amdgcn_sched_barrier(0);
       const int m = tile_m * BM + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+      if constexpr (GU && TN == 1) {
+        const float v = acc[i][0][e];
+        const float other = __shfl_xor(v, 16);  // every lane, before any lane leaves
+        if (m >= g.M) continue;
+        const int f = tile_n * (BN / 2) + wn * 16 + (fr & 15);
+        if (f >= g.N) continue;
+        if (split) {
+          float* row = g.part + ((size_t)slice * g.M + m) * (size_t)(2 * g.N);
+          row[(fr < 16 ? 0 : g.N) + f] = v;
+        } else if (fr < 16) {
+          put_h(g.out, g.M, g.ldh, m, f, silu_mul(v, other), g.h_planes);
+        }
+        continue;
+      }
       if (m >= g.M) continue;
       if (GU) {
 #pragma unroll
@@ -358,7 +374,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
 #define SMLP_GEMM_CONFIGS(X)                                                                    \
   X(256, 256, 2, 4, 2) X(128, 256, 2, 4, 3) X(128, 256, 2, 2, 3) X(128, 128, 2, 2, 2)           \
   X(128, 128, 2, 2, 4) X(128, 128, 4, 2, 4) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4) X(128, 64, 4, 1, 6) \
-  X(128, 128, 4, 2, 2) X(128, 128, 4, 2, 3) X(128, 256, 2, 4, 2) X(256, 128, 4, 2, 2) X(256, 128, 4, 2, 3)
+  X(128, 128, 4, 2, 2) X(128, 128, 4, 2, 3) X(128, 256, 2, 4, 2) X(256, 128, 4, 2, 2) X(256, 128, 4, 2, 3) \
+  X(128, 64, 4, 2, 3) X(128, 64, 4, 2, 4)
 // Down only (one MFMA tile column per wave cannot pair gate and up rows).
 #define SMLP_GEMM_DN_CONFIGS(X) X(128, 32, 4, 1, 2) X(128, 32, 4, 1, 4) X(64, 64, 2, 2, 4)
 #define SMLP_GEMM_HILO_CONFIGS(X) X(128, 128, 2, 2, 3) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4)
