@@ -24,7 +24,7 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
 
 /* The LDS-tiled (large-M) stages (stage 2: the plain projection, planned like down):
  * tile of bm tokens x bn weight rows (0 and 0 =
- * automatic; bm in {64 (down only, with bn 64 on a 2 x 2 wave grid), 128, 256}, bn in
+ * automatic; bm in {64 (with bn 64 on a 2 x 2 wave grid), 128, 256}, bn in
  * {32 (down only), 64, 128, 256}), the wave grid
  * wm x wn over the tile (0 and 0 = automatic; each in {1, 2, 4}), the number of LDS
  * stages ns (0 = automatic, <= 8) and the K split over workgroups (0 = automatic,

@@ -375,9 +375,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   X(256, 256, 2, 4, 2) X(128, 256, 2, 4, 3) X(128, 256, 2, 2, 3) X(128, 128, 2, 2, 2)           \
   X(128, 128, 2, 2, 4) X(128, 128, 4, 2, 4) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4) X(128, 64, 4, 1, 6) \
   X(128, 128, 4, 2, 2) X(128, 128, 4, 2, 3) X(128, 256, 2, 4, 2) X(256, 128, 4, 2, 2) X(256, 128, 4, 2, 3) \
-  X(128, 64, 4, 2, 3) X(128, 64, 4, 2, 4)
+  X(128, 64, 4, 2, 3) X(128, 64, 4, 2, 4) X(64, 64, 2, 2, 4)
 // Down only (one MFMA tile column per wave cannot pair gate and up rows).
-#define SMLP_GEMM_DN_CONFIGS(X) X(128, 32, 4, 1, 2) X(128, 32, 4, 1, 4) X(64, 64, 2, 2, 4)
+#define SMLP_GEMM_DN_CONFIGS(X) X(128, 32, 4, 1, 2) X(128, 32, 4, 1, 4)
 #define SMLP_GEMM_HILO_CONFIGS(X) X(128, 128, 2, 2, 3) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4)
 
 template <int MODE>

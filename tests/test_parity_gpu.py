@@ -332,8 +332,8 @@ GATE_UP_TILES = [(256, 256, 2, 4, 2), (128, 256, 2, 4, 3), (128, 256, 2, 2, 3), 
                  (128, 128, 2, 2, 2), (128, 128, 2, 2, 4), (128, 128, 4, 2, 2), (128, 128, 4, 2, 3),
                  (128, 128, 4, 2, 4), (256, 128, 4, 2, 2), (256, 128, 4, 2, 3),
                  (128, 64, 4, 1, 2), (128, 64, 4, 1, 4), (128, 64, 4, 1, 6), (128, 64, 4, 2, 3),
-                 (128, 64, 4, 2, 4)]
-DOWN_TILES = GATE_UP_TILES + [(128, 32, 4, 1, 2), (128, 32, 4, 1, 4), (64, 64, 2, 2, 4)]
+                 (128, 64, 4, 2, 4), (64, 64, 2, 2, 4)]
+DOWN_TILES = GATE_UP_TILES + [(128, 32, 4, 1, 2), (128, 32, 4, 1, 4)]
 
 
 @pytest.mark.parametrize("ksplit", [1, 3])
