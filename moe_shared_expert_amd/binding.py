@@ -79,6 +79,13 @@ LAYOUT_EXPORTS = {
     "shared_mlp_choose_layout": (_int, [ctypes.POINTER(LayoutModel), _i64, ctypes.POINTER(_int)]),
     "shared_mlp_layout_crossover": (_int, [ctypes.POINTER(LayoutModel), _i64, ctypes.POINTER(_i64)]),
 }
+# declared in include/smlp_ceilings.h
+CEILING_EXPORTS = {
+    "shared_mlp_ceiling_empty": (_int, [_int, _vp]),
+    "shared_mlp_ceiling_read": (_int, [_vp, _sz, _int, _sz, _int, _vp, _vp]),
+    "shared_mlp_ceiling_mfma": (_int, [_int, _int, _vp, _vp, _vp, _vp]),
+    "shared_mlp_ceiling_two_phase": (_int, [_vp, _sz, _int, _sz, _int, _vp, _vp, _vp]),
+}
 # declared in include/smlp_tuning.h
 TUNING_EXPORTS = {
     "shared_mlp_tune_skinny": (_int, [_int, _int, _int, _int, _int, _int]),
@@ -95,7 +102,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m moe_shared_expert_amd.build` (no fallback exists)")
         L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in {**EXPORTS, **TUNING_EXPORTS, **LAYOUT_EXPORTS}.items():
+        for name, (res, args) in {**EXPORTS, **TUNING_EXPORTS, **LAYOUT_EXPORTS, **CEILING_EXPORTS}.items():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
@@ -161,6 +168,34 @@ def _shapes(x, w_gate_up, w_down, out):
     return M, H, I
 
 
+def _out_dtype(x_dtype, partial_fp32):
+    """The output element type the library writes: fp32 for a partial or fp32 inputs, else bf16."""
+    return torch.float32 if (partial_fp32 or x_dtype == torch.float32) else torch.bfloat16
+
+
+def _check_types(x, weights, out, partial_fp32):
+    """The library cannot see buffer sizes, so element types are checked here: every
+    weight has x's dtype and out has the dtype the kernels write (a mismatch would make
+    them read or write past the end of a buffer)."""
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"x dtype {x.dtype} is neither bfloat16 nor float32")
+    for name, w in weights:
+        if w is not None and w.dtype != x.dtype:
+            raise TypeError(f"{name} dtype {w.dtype} differs from x dtype {x.dtype}")
+    if out is not None:
+        want = _out_dtype(x.dtype, partial_fp32)
+        if out.dtype != want:
+            raise TypeError(f"out dtype {out.dtype}: the kernels write {want} here "
+                            f"(partial_fp32={bool(partial_fp32)}, x {x.dtype})")
+    for name, t in (("x", x), *weights, ("out", out)):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+
+
+def _ws_bytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def _workspace(workspace, M, H, I, dtype, device):
     need = shared_mlp_workspace_bytes(M, H, I, dtype)
     if workspace is None:
@@ -171,27 +206,36 @@ def _workspace(workspace, M, H, I, dtype, device):
 def shared_mlp_forward(x, w_gate_up, w_down, out, partial_fp32=False, workspace=None, stream=None):
     """out = down(SiLU(x Wg^T) * (x Wu^T)); out is bf16, or fp32 for partial_fp32 / fp32 inputs."""
     M, H, I = _shapes(x, w_gate_up, w_down, out)
+    _check_types(x, (("w_gate_up", w_gate_up), ("w_down", w_down)), out, partial_fp32)
     dt = _dtype_code(x)
     workspace = _workspace(workspace, M, H, I, dt, x.device)
     _check(lib().shared_mlp_forward(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), M, H, I, dt,
-                                    int(bool(partial_fp32)), _ptr(workspace), workspace.numel(),
+                                    int(bool(partial_fp32)), _ptr(workspace), _ws_bytes(workspace),
                                     _stream(stream, x.device)))
     return out
 
 
 def shared_mlp_gate_up_act(x, w_gate_up, workspace, partial_fp32=False, stream=None):
     M, H, I = _shapes(x, w_gate_up, None, None)
+    _check_types(x, (("w_gate_up", w_gate_up),), None, partial_fp32)
     dt = _dtype_code(x)
     _check(lib().shared_mlp_gate_up_act(_ptr(x), _ptr(w_gate_up), M, H, I, dt, int(bool(partial_fp32)),
-                                        _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
+                                        _ptr(workspace), _ws_bytes(workspace), _stream(stream, x.device)))
 
 
 def shared_mlp_down(w_down, out, workspace, partial_fp32=False, stream=None):
     H, I = w_down.shape
+    if out.dim() != 2 or out.shape[1] != H:
+        raise ValueError(f"out {tuple(out.shape)} must be [M, {H}] for w_down {tuple(w_down.shape)}")
     M = out.shape[0]
     dt = _dtype_code(w_down)
+    want = _out_dtype(w_down.dtype, partial_fp32)
+    if out.dtype != want:
+        raise TypeError(f"out dtype {out.dtype}: the down kernels write {want} here")
+    if out.device != w_down.device:
+        raise ValueError(f"out is on {out.device}, w_down on {w_down.device}")
     _check(lib().shared_mlp_down(_ptr(w_down), _ptr(out), M, H, I, dt, int(bool(partial_fp32)),
-                                 _ptr(workspace), workspace.numel(), _stream(stream, w_down.device)))
+                                 _ptr(workspace), _ws_bytes(workspace), _stream(stream, w_down.device)))
 
 
 def read_h(workspace, M: int, I: int, H: int, dtype: int = SMLP_BF16, partial_fp32=False):
@@ -247,6 +291,16 @@ def shared_mlp_slice_rank(w_gate_up, w_down, w_gate_up_r, w_down_r, tp: int, ran
     two_i, H = w_gate_up.shape
     I = two_i // 2
     dt = _dtype_code(w_gate_up)
+    if tuple(w_down.shape) != (H, I):
+        raise ValueError(f"w_down {tuple(w_down.shape)} != ({H}, {I})")
+    if tp >= 1 and I % tp == 0:
+        s = I // tp
+        if tuple(w_gate_up_r.shape) != (2 * s, H) or tuple(w_down_r.shape) != (H, s):
+            raise ValueError(f"slice destinations {tuple(w_gate_up_r.shape)}, {tuple(w_down_r.shape)} must be "
+                             f"({2 * s}, {H}) and ({H}, {s})")
+    for name, t in (("w_down", w_down), ("w_gate_up_r", w_gate_up_r), ("w_down_r", w_down_r)):
+        if t.dtype != w_gate_up.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from w_gate_up dtype {w_gate_up.dtype}")
     _check(lib().shared_mlp_slice_rank(_ptr(w_gate_up), _ptr(w_down), _ptr(w_gate_up_r), _ptr(w_down_r),
                                        H, I, tp, rank, dt, _stream(stream, w_gate_up.device)))
 
@@ -290,7 +344,7 @@ def shared_mlp_linear(x, w, y, workspace=None, stream=None):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(lib().shared_mlp_linear(_ptr(x), _ptr(w), y.data_ptr(), M, K, N, ldy, int(y.dtype == torch.float32),
                                    _ptr(workspace) if workspace is not None else None,
-                                   workspace.numel() if workspace is not None else 0,
+                                   _ws_bytes(workspace),
                                    _stream(stream, x.device)))
     return y
 
@@ -340,13 +394,44 @@ def shared_mlp_layout_crossover(model, T_max: int) -> int:
 def shared_mlp_forward_rank(x, w_gate_up, w_down, out, tp: int, rank: int, workspace=None, stream=None):
     """Rank `rank`'s fp32 partial computed in place from the full weights (no shard copy)."""
     M, H, I = _shapes(x, w_gate_up, w_down, out)
+    _check_types(x, (("w_gate_up", w_gate_up), ("w_down", w_down)), out, True)
     dt = _dtype_code(x)
-    if out.dtype != torch.float32:
-        raise TypeError("the rank partial is fp32")
     if workspace is None:
         need = shared_mlp_workspace_bytes(M, H, I // tp if tp > 0 and I % tp == 0 else I, dt)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _check(lib().shared_mlp_forward_rank(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), M, H, I, int(tp),
-                                         int(rank), dt, _ptr(workspace), workspace.numel(),
+                                         int(rank), dt, _ptr(workspace), _ws_bytes(workspace),
                                          _stream(stream, x.device)))
     return out
+
+
+# Measurement kernels (include/smlp_ceilings.h): launch them, time them on the caller's side.
+
+def ceiling_empty(blocks: int = 256, stream=None):
+    _check(lib().shared_mlp_ceiling_empty(int(blocks), _stream(stream, torch.device("cuda"))))
+
+
+def ceiling_read(src, blocks: int, bytes_per_block: int, shared: bool, sink, stream=None):
+    """Streaming read of src (a uint8/any GPU tensor) by `blocks` workgroups; see the header."""
+    _check(lib().shared_mlp_ceiling_read(_ptr(src), src.numel() * src.element_size(), int(blocks),
+                                         int(bytes_per_block), int(bool(shared)), _ptr(sink),
+                                         _stream(stream, src.device)))
+
+
+def ceiling_mfma(blocks: int, iters: int, sink, cycles, ticks, stream=None):
+    if sink.dtype != torch.float32 or cycles.dtype != torch.int64 or ticks.dtype != torch.int64:
+        raise TypeError("sink is fp32, cycles and ticks int64")
+    if min(sink.numel(), cycles.numel(), ticks.numel()) < blocks:
+        raise ValueError("sink, cycles and ticks need one element per block")
+    _check(lib().shared_mlp_ceiling_mfma(int(blocks), int(iters), _ptr(sink), _ptr(cycles), _ptr(ticks),
+                                         _stream(stream, sink.device)))
+
+
+def ceiling_two_phase(src, blocks: int, bytes_per_block: int, barrier: bool, bar_state, sink, stream=None):
+    if bar_state.dtype != torch.int32 or bar_state.numel() < 4:
+        raise TypeError("bar_state is 4 int32")
+    if sink.dtype != torch.float32 or sink.numel() < blocks:
+        raise ValueError("sink needs one fp32 per block")
+    _check(lib().shared_mlp_ceiling_two_phase(_ptr(src), src.numel() * src.element_size(), int(blocks),
+                                              int(bytes_per_block), int(bool(barrier)), _ptr(bar_state),
+                                              _ptr(sink), _stream(stream, src.device)))

@@ -127,6 +127,24 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
       nt = 4;
       fpw = 4 * tile;
     }
+    // Without a pinned tile count, narrow the workgroups (more of them) until some
+    // compiled (waves, stages) pair serves the tile count: not every (tokens, tiles)
+    // combination is instantiated (two token tiles take at most 2 tiles per workgroup in
+    // the projection kernel, for one).
+    if (!o.nb.load()) {
+      auto served = [&](int64_t t) {
+        for (int w : {4, 8})
+          for (int st = 2; st <= 8; ++st)
+            if (smlp::skinny_instantiated(inst, sp.kind, sp.mt, (int)t, o.waves.load() ? o.waves.load() : w,
+                                          o.u.load() ? o.u.load() : st))
+              return true;
+        return false;
+      };
+      while (nt > 1 && !served(nt)) {
+        --nt;
+        fpw = nt * tile;
+      }
+    }
     groups = (N + fpw - 1) / fpw;
     sp.nb = (int)nt;
     sp.fpw = (int)fpw;
@@ -151,6 +169,16 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
           break;
         }
       }
+    }
+    if (!sp.waves && !(o.waves.load() && o.u.load())) {
+      // none of the measured preferences is compiled for this tile count: take any pair
+      for (int w : {4, 8})
+        for (int st = 2; st <= 8 && !sp.waves; ++st)
+          if (smlp::skinny_instantiated(inst, sp.kind, sp.mt, (int)nt, o.waves.load() ? o.waves.load() : w,
+                                        o.u.load() ? o.u.load() : st)) {
+            sp.waves = o.waves.load() ? o.waves.load() : w;
+            sp.u = o.u.load() ? o.u.load() : st;
+          }
     }
     if (o.waves.load()) sp.waves = o.waves.load();
     if (o.u.load()) sp.u = o.u.load();

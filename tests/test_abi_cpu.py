@@ -46,9 +46,13 @@ def test_every_declared_symbol_is_exported(L):
     for n in layout:
         assert hasattr(L, n), n
     assert set(layout) == set(binding.LAYOUT_EXPORTS)
+    ceil = _declared("smlp_ceilings.h")
+    for n in ceil:
+        assert hasattr(L, n), n
+    assert set(ceil) == set(binding.CEILING_EXPORTS)
     # every header under include/ is covered above
     assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(
-        ["smlp.h", "smlp_latent.h", "smlp_layout.h", "smlp_tuning.h"])
+        ["smlp.h", "smlp_latent.h", "smlp_layout.h", "smlp_tuning.h", "smlp_ceilings.h"])
 
 
 def test_tuning_hook(L):

@@ -32,7 +32,8 @@ def run_forward(x, wgu, wd, partial=False):
     Ii = wgu.shape[0] // 2
     dt = binding.SMLP_FP32 if x.dtype == torch.float32 else binding.SMLP_BF16
     odt = torch.float32 if (partial or x.dtype == torch.float32) else torch.bfloat16
-    out = torch.empty(M, Hh, dtype=odt, device=DEV)
+    # NaN-filled, so that an output element the kernels never write fails the comparison
+    out = torch.full((M, Hh), float("nan"), dtype=odt, device=DEV)
     ws = workspace_for(M, Hh, Ii, dt)
     binding.shared_mlp_forward(x, wgu, wd, out, partial_fp32=partial, workspace=ws)
     torch.cuda.synchronize()
@@ -181,6 +182,66 @@ def test_stack92_every_layer_on_seeded_input(stack92, chunk):
         assert_rms_close(out, ref, BF16_TOL, f"stack92 layer{l}")
 
 
+@pytest.fixture(scope="module")
+def oracle_chain(stack92):
+    """The 92-layer chain run by the oracle alone from the seeded x_0: layer l's fp64
+    output, rescaled per token to unit RMS (oracle.rms_rescale_rows) and stored as bf16
+    (round to nearest even, the storage conversion of the inputs), is layer l + 1's
+    input.  Returns every layer's bf16 input and fp64 output."""
+    x = synth.activations(128, H, config=4)
+    xs, outs = [], []
+    for wgu, wd in stack92:
+        out = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+        xs.append(x)
+        outs.append(out)
+        x = torch.from_numpy(oracle.rms_rescale_rows(out)).to(torch.float32).to(torch.bfloat16)
+    return xs, outs
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_stack92_chain_layers_on_oracle_inputs(stack92, oracle_chain, chunk):
+    # Every layer of the chain on the input distribution the chain produces: the GPU layer
+    # l runs on the oracle chain's x_l (no input comes from the GPU) and must match the
+    # oracle's layer-l output; the GPU rescale of the GPU output must match the oracle's
+    # rescale of that same output to one bf16 rounding.
+    xs, outs = oracle_chain
+    ws = workspace_for(128, H, 384, binding.SMLP_BF16)
+    for l in range(chunk * 23, (chunk + 1) * 23):
+        wgu, wd = stack92[l]
+        out = torch.full((128, H), float("nan"), dtype=torch.float32, device=DEV)
+        binding.shared_mlp_forward(xs[l].to(DEV), wgu.to(DEV), wd.to(DEV), out, partial_fp32=True, workspace=ws)
+        nxt = torch.empty(128, H, dtype=torch.bfloat16, device=DEV)
+        binding.shared_mlp_rms_rescale(out, nxt)
+        torch.cuda.synchronize()
+        assert_rms_close(out, outs[l], BF16_TOL, f"stack92 chain layer{l} on the oracle's input")
+        ref = oracle.rms_rescale_rows(f64(out))
+        err = np.abs(f64(nxt) - ref) / np.maximum(np.abs(ref), 1e-30)
+        assert err.max() <= 2.0 ** -8 * 1.01, (l, err.max())
+
+
+# The free-running GPU chain departs from the oracle chain by rounding alone: a CPU
+# emulation of the kernels' arithmetic (bf16 operands, fp32 sums, h rounded to bf16 once)
+# gives max|diff| / RMS of 1.1e-2, 2.3e-2, 3.6e-2, 6.1e-2, 9.8e-2 at layers 0-4 (growing
+# about 1.6x per layer, O(1) by layer 10).  Layer 0 is held to the parity bar; layers 1-4 to
+# the envelope 2e-2 * 2^l, which a wrong or stale layer input (an O(1) error) breaks at once.
+CHAIN_LAYERS = 5
+
+
+def test_stack92_free_running_chain_tracks_oracle(stack92, oracle_chain):
+    _, outs = oracle_chain
+    x = synth.activations(128, H, config=4).to(DEV)
+    ws = workspace_for(128, H, 384, binding.SMLP_BF16)
+    for l in range(CHAIN_LAYERS):
+        wgu, wd = stack92[l]
+        out = torch.full((128, H), float("nan"), dtype=torch.float32, device=DEV)
+        binding.shared_mlp_forward(x, wgu.to(DEV), wd.to(DEV), out, partial_fp32=True, workspace=ws)
+        nxt = torch.empty(128, H, dtype=torch.bfloat16, device=DEV)
+        binding.shared_mlp_rms_rescale(out, nxt)
+        torch.cuda.synchronize()
+        assert_rms_close(out, outs[l], BF16_TOL * 2 ** l, f"stack92 free-running chain layer{l}")
+        x = nxt
+
+
 def test_stack92_chain_properties(stack92):
     # The chained run (output rescaled to unit RMS feeds the next layer).  The chain
     # amplifies rounding differences, so it is checked by properties at every layer:
@@ -217,19 +278,15 @@ def test_rms_rescale_against_oracle(Hh):
 
 
 # ------------------------------------------------------------ prefill, M = 8192
-SAMPLE_ROWS = [0, 1, 2, 15, 16, 127, 128, 129, 1000, 4095, 4096, 8190, 8191] + list(range(3001, 8000, 419))
-
-
-def test_prefill_m8192_sampled_rows(full_layer):
+def test_prefill_m8192_every_row(full_layer):
+    # the whole [8192, 7168] output (NaN-filled before the call) against the fp64 oracle
     wgu, wd, wgu64, wd64 = full_layer
     x = synth.activations(8192, H, config=5)
     p = binding.shared_mlp_plan(8192, H, I)
     assert p["path_name"] == "large_m"
     out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
-    rows = np.array(SAMPLE_ROWS)
-    ref = oracle.swiglu_mlp(f64(x[rows]), wgu64, wd64)
-    # RMS of the oracle over the sampled rows stands in for the full-output RMS
-    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, "prefill M=8192 sampled")
+    ref = oracle.swiglu_mlp(f64(x), wgu64, wd64)
+    assert_rms_close(out, ref, BF16_TOL, "prefill M=8192 all rows")
 
 
 @pytest.mark.parametrize("partial", [False, True])
@@ -242,9 +299,8 @@ def test_down_column_split_ragged(partial):
     x = synth.activations(M, Hh, config=13)
     wgu, wd = synth.layer_weights(Hh, Ii, config=13)
     out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=partial)
-    rows = np.array([0, 1, 127, 128, 4095, 4096, 8063, 8064, 8099])
-    ref = oracle.swiglu_mlp(f64(x[rows]), f64(wgu), f64(wd))
-    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"column split partial={partial}")
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, f"column split partial={partial}")
 
 
 def test_gate_up_column_split_ragged():
@@ -258,9 +314,8 @@ def test_gate_up_column_split_ragged():
     x = synth.activations(M, Hh, config=14)
     wgu, wd = synth.layer_weights(Hh, Ii, config=14)
     out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
-    rows = np.array([0, 1, 127, 128, 255, 256, 1023, 1791, 1792, 1999])
-    ref = oracle.swiglu_mlp(f64(x[rows]), f64(wgu), f64(wd))
-    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, "gate_up column split")
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, "gate_up column split")
 
 
 # ---------------------------------------------- M sweep, replicated and TP8 shard
@@ -269,9 +324,8 @@ def test_sweep_replicated(M, full_layer):
     wgu, wd, wgu64, wd64 = full_layer
     x = synth.activations(M, H, config=5, copy=M)
     out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
-    rows = np.arange(M) if M <= 512 else np.array(sorted(set([0, M - 1] + list(range(1, M, M // 24)))))
-    ref = oracle.swiglu_mlp(f64(x[rows]), wgu64, wd64)
-    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"sweep rep M={M}")
+    ref = oracle.swiglu_mlp(f64(x), wgu64, wd64)
+    assert_rms_close(out, ref, BF16_TOL, f"sweep rep M={M}")
 
 
 @pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 2048])
@@ -281,9 +335,8 @@ def test_sweep_tp8(M, full_layer):
     x = synth.activations(M, H, config=5, copy=10000 + M)
     wgu_r, wd_r = slice_on_gpu(wgu.to(DEV), wd.to(DEV), 8, 5)
     out = run_forward(x.to(DEV), wgu_r, wd_r, partial=True)
-    rows = np.arange(M) if M <= 512 else np.array(sorted(set([0, M - 1] + list(range(1, M, M // 24)))))
-    ref = oracle.swiglu_mlp(f64(x[rows]), g_r, d_r)
-    assert_rms_close(out[torch.from_numpy(rows).to(DEV)], ref, BF16_TOL, f"sweep tp8 M={M}")
+    ref = oracle.swiglu_mlp(f64(x), g_r, d_r)
+    assert_rms_close(out, ref, BF16_TOL, f"sweep tp8 M={M}")
 
 
 # ------------------------------------------------------------------ edge cases
@@ -296,6 +349,19 @@ def test_ragged_m_medium_shapes(M, partial):
     out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=partial)
     ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
     assert_rms_close(out, ref, BF16_TOL, f"ragged M={M} partial={partial}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("M,Hh,Ii", [(65, 1024, 768), (100, 1024, 768), (128, 1024, 768), (128, 2048, 1536),
+                                     (96, 2048, 1536)])
+def test_medium_shapes_bf16_out_over_seeds(M, Hh, Ii, seed):
+    # the family with the least parity margin (bf16 output, medium M, H and I): eight
+    # seeds per shape, on the default path for that M
+    x = synth.activations(M, Hh, config=15, copy=seed)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=15, copy=seed)
+    out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(out, ref, BF16_TOL, f"medium bf16 M={M} H={Hh} I={Ii} seed={seed}")
 
 
 @pytest.mark.parametrize("Hh,Ii", [(136, 40), (72, 8), (8, 24), (520, 1000)])
