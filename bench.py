@@ -197,7 +197,8 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
     out_elem = 4 if partial else 2
     alg = roofline.algorithmic_bytes(M, H, I_r, 2, out_elem)
     fl = roofline.flops(M, H, I_r)
-    h_elem = {binding.SMLP_FP32: 4, binding.SMLP_BF16_HILO: 4, binding.SMLP_BF16: 2}[plan["h_dtype"]]
+    h_elem = {binding.SMLP_FP32: 4, binding.SMLP_BF16_HILO: 4, binding.SMLP_BF16: 2,
+              binding.SMLP_FP16: 2}[plan["h_dtype"]]
     gu_alg = roofline.gate_up_bytes(H, I_r) + M * H * 2 + M * I_r * h_elem
     us = median(layer)
     gu_us = median(gu)

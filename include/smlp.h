@@ -50,9 +50,10 @@
 extern "C" {
 #endif
 
-/* Element types.  SMLP_BF16_HILO only describes the intermediate h in a workspace:
- * two bf16 planes [M, I] (hi first, then lo) whose sum is the fp32 value. */
-enum { SMLP_BF16 = 0, SMLP_FP32 = 1, SMLP_BF16_HILO = 2 };
+/* Element types.  SMLP_BF16_HILO and SMLP_FP16 only describe the intermediate h in a
+ * workspace: two bf16 planes [M, I] (hi first, then lo) whose sum is the fp32 value, or
+ * one fp16 plane [M, I] (rounded once to nearest even; |h| must stay below 65504). */
+enum { SMLP_BF16 = 0, SMLP_FP32 = 1, SMLP_BF16_HILO = 2, SMLP_FP16 = 3 };
 
 /* Status codes. */
 enum {

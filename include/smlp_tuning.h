@@ -39,6 +39,14 @@ int shared_mlp_tune_gemm(int stage, int bm, int bn, int wm, int wn, int ns, int 
  * Process-wide, for subsequent plans.  Returns SMLP_OK or SMLP_ERR_ARG. */
 int shared_mlp_tune_h_planes(int planes);
 
+/* Format of the intermediate h on the LDS-tiled (large-M) path: 0 = automatic (two bf16
+ * planes hi + lo when I < 256, else one fp16 plane for a bf16 output and one bf16 plane
+ * for an fp32 partial), 1 = one bf16 plane, 2 = two bf16 planes, 3 = one fp16 plane.  One bf16 plane rounds h to 8 significant bits, which can
+ * take a bf16-output layer past the parity bound over a large output; it is here for
+ * timing comparisons.  Process-wide, for subsequent plans.  Returns SMLP_OK or
+ * SMLP_ERR_ARG. */
+int shared_mlp_tune_h_format(int fmt);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,7 @@ import os
 
 import torch
 
-SMLP_BF16, SMLP_FP32, SMLP_BF16_HILO = 0, 1, 2
+SMLP_BF16, SMLP_FP32, SMLP_BF16_HILO, SMLP_FP16 = 0, 1, 2, 3
 PATH_NAMES = {0: "none", 1: "fp32", 2: "small_m", 3: "large_m"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +91,7 @@ TUNING_EXPORTS = {
     "shared_mlp_tune_skinny": (_int, [_int, _int, _int, _int, _int, _int]),
     "shared_mlp_tune_gemm": (_int, [_int, _int, _int, _int, _int, _int, _int]),
     "shared_mlp_tune_h_planes": (_int, [_int]),
+    "shared_mlp_tune_h_format": (_int, [_int]),
 }
 
 
@@ -248,6 +249,8 @@ def read_h(workspace, M: int, I: int, H: int, dtype: int = SMLP_BF16, partial_fp
     if p["h_dtype"] == SMLP_BF16_HILO:
         planes = workspace[o:o + 4 * M * I].view(torch.bfloat16).view(2, M, I)
         return planes[0].float() + planes[1].float()
+    if p["h_dtype"] == SMLP_FP16:
+        return workspace[o:o + 2 * M * I].view(torch.float16).view(M, I)
     return workspace[o:o + 2 * M * I].view(torch.bfloat16).view(M, I)
 
 
@@ -266,6 +269,11 @@ def shared_mlp_tune_gemm(stage: int, bm: int = 0, bn: int = 0, wm: int = 0, wn: 
 def shared_mlp_tune_h_planes(planes: int = 0):
     """Planes of h on the small-M path (0 = automatic); see include/smlp_tuning.h."""
     _check(lib().shared_mlp_tune_h_planes(planes))
+
+
+def shared_mlp_tune_h_format(fmt: int = 0):
+    """Format of h on the large-M path (0 = automatic); see include/smlp_tuning.h."""
+    _check(lib().shared_mlp_tune_h_format(fmt))
 
 
 def forward(x, w_gate_up, w_down, partial_fp32=False, workspace=None, stream=None):

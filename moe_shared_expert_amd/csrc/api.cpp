@@ -78,6 +78,8 @@ GemmOverride g_gtune[3];
 // Planes of h on the small-M path (0 = automatic: one for M <= 32 and I >= 256, else
 // two), see shared_mlp_tune_h_planes.
 std::atomic<int> g_h_planes{0};
+// Format of h on the large-M path (0 = automatic), see shared_mlp_tune_h_format.
+std::atomic<int> g_h_format{0};
 
 // Small-M stage plan.  M <= 32: the streaming kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
@@ -492,9 +494,18 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     p->kernels = 2 + (p->gu.ksplit > 1) + (p->dn.ksplit > 1);
   } else {
     p->path = SMLP_PATH_LARGE_M;
-    // one bf16 plane; two (hi + lo) when the down contraction is too short (I < 256)
-    // for the rounding of h to average out
-    p->h_dtype = I < 256 ? SMLP_BF16_HILO : SMLP_BF16;
+    // h for a bf16 output: one fp16 plane (the down stage converts its bf16 weight
+    // fragments to fp16 in registers, exactly, and multiplies with fp16 MFMAs), rounded
+    // with 11 significant bits instead of bf16's 8: with one bf16 plane, h's rounding on
+    // top of the output's own rounding took the whole-output error to 0.94-1.01 of the
+    // bound at M = 8100...8192 and 0.93 on medium shapes.  For an fp32 output (a TP
+    // rank's partial, no output rounding) one bf16 plane keeps the error near 0.7 of the
+    // bound and spares the conversion (5-14% of the down GEMM).  Two bf16 planes (hi +
+    // lo) when the down contraction is too short (I < 256) for the rounding of h to
+    // average out.
+    const int hf = g_h_format.load();
+    p->h_dtype = hf == 1 ? SMLP_BF16 : hf == 2 ? SMLP_BF16_HILO : hf == 3 ? SMLP_FP16
+               : I < 256 ? SMLP_BF16_HILO : partial_fp32 ? SMLP_BF16 : SMLP_FP16;
     p->h_bytes = round_up((size_t)(M * I) * (p->h_dtype == SMLP_BF16_HILO ? 4 : 2), 256);
     const bool hilo = p->h_dtype == SMLP_BF16_HILO;
     // Only the down stage reads h; its two-plane form has its own tile list.
@@ -935,6 +946,12 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
 int shared_mlp_tune_h_planes(int planes) {
   if (planes < 0 || planes > 2) return fail(SMLP_ERR_ARG, "planes = %d outside {0, 1, 2}", planes);
   g_h_planes = planes;
+  return ok();
+}
+
+int shared_mlp_tune_h_format(int fmt) {
+  if (fmt < 0 || fmt > 3) return fail(SMLP_ERR_ARG, "fmt = %d outside {0, 1, 2, 3}", fmt);
+  g_h_format = fmt;
   return ok();
 }
 

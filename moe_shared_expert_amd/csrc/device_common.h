@@ -6,6 +6,7 @@
 namespace smlp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -46,6 +47,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D += A * B for one 32x32x16 fp16 tile (same lane layout as the bf16 form).
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+
+// Eight bf16 values -> eight fp16 values, element order kept.  Every bf16 value in the
+// fp16 normal range is exactly representable (8 significant bits of 11), so the
+// conversion is exact there; smaller magnitudes round toward zero to a multiple of
+// 2^-24 and magnitudes past 65504 saturate to 65504 (neither occurs for weights).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[j] << 16),
+                                                                  __uint_as_float(v[j] & 0xffff0000u)));
+  return r;
+}
+
+// fp32 -> fp16 bits, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint32_t f2h(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
 // Buffer resource over [base, base + bytes) for raw buffer loads; a load whose offset

@@ -19,9 +19,12 @@
 //
 // gate_up: the B rows of each wave hold a block of gate rows followed by the matching
 // up rows, so a feature's gate and up sums land in the same lane and element of two
-// MFMA tiles and SiLU-and-mul is a register operation.  down: A is h as one bf16 plane,
-// or as two planes hi + lo (two MFMAs per fragment).  With a K split over workgroups
-// the raw fp32 sums go to a partial buffer and a finalize kernel applies the epilogue.
+// MFMA tiles and SiLU-and-mul is a register operation.  down: A is h as one fp16 plane
+// (the weight fragments are converted from bf16 to fp16 after their LDS read, exactly,
+// and multiplied with fp16 MFMAs of the same rate), as one bf16 plane (the plain
+// projection, A = x), or as two bf16 planes hi + lo (two MFMAs per fragment).  With a K
+// split over workgroups the raw fp32 sums go to a partial buffer and a finalize kernel
+// applies the epilogue.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2; the
 // (K slice, tile) order gives each XCD a contiguous run, walked in groups of GROUP_M
@@ -36,7 +39,7 @@ namespace smlp {
 namespace {
 
 
-enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2 };
+enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2, GM_DOWN_F16 = 3 };
 
 struct GArgs {
   const uint16_t* a;      // [M, K] bf16 (down, two planes: hi)
@@ -53,19 +56,26 @@ struct GArgs {
   int ldo;                // down: elements between output rows (>= N)
   float* part;            // gridDim.y > 1: fp32 partial sums [slices][M][P*N]
   int out_f32;
-  int h_planes;           // gate_up: planes of h to store (1 or 2)
+  int h_fmt;              // gate_up: h as one bf16 plane (1), bf16 hi + lo (2) or fp16 (3)
   int ldh;                // gate_up: elements between rows of h (>= N; planes are M * ldh apart)
 };
+
+// Format code of h in the kernels: one bf16 plane (1), bf16 hi + lo (2), fp16 (3).
+int h_format(int h_dtype) { return h_dtype == SMLP_BF16_HILO ? 2 : h_dtype == SMLP_FP16 ? 3 : 1; }
 
 constexpr int BK = 64;      // K elements per step (128 bytes of a row)
 constexpr int GROUP_M = 8;  // token tiles per group in the tile order
 constexpr int XCDS = 8;
 
-__device__ __forceinline__ void put_h(void* base, int M, int ld, int m, int n, float h, int planes) {
-  const uint32_t hi = f2bf(h);
+__device__ __forceinline__ void put_h(void* base, int M, int ld, int m, int n, float h, int fmt) {
   uint16_t* p = reinterpret_cast<uint16_t*>(base);
+  if (fmt == 3) {
+    p[(size_t)m * ld + n] = (uint16_t)f2h(h);
+    return;
+  }
+  const uint32_t hi = f2bf(h);
   p[(size_t)m * ld + n] = (uint16_t)hi;
-  if (planes == 2) p[(size_t)M * ld + (size_t)m * ld + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
+  if (fmt == 2) p[(size_t)M * ld + (size_t)m * ld + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
 }
 
 // Swizzle of the 16-byte chunks within tile row r.
@@ -122,6 +132,7 @@ __device__ __forceinline__ void wait_steps(int later) {
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   constexpr bool GU = MODE == GM_GATE_UP;
+  constexpr bool F16 = MODE == GM_DOWN_F16;
   constexpr int NA = MODE == GM_DOWN_HILO ? 2 : 1;
   constexpr int W = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
@@ -223,6 +234,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   // 1175 us, down 674 -> 657 us).  Thinner wave tiles, with too few MFMAs to hide the
   // reads behind, keep the compiler's schedule (measured slightly faster there).
   constexpr bool PINNED = NMFMA >= NFRAG;
+  auto mma = [](u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (F16) return mfma32x32x16_f16(a, b, c);
+    else return mfma32x32x16(a, b, c);
+  };
   auto compute = [&](int buf, auto&& hook) {
     const char* st = lds + buf * STAGE;
     u32x4 fa[2][NA][TM], fb[2][TN];
@@ -247,12 +262,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
 #pragma unroll
           for (int t = 0; t < NFRAG; ++t) read_frag(cur ^ 1, ks + 1, t);
         }
+        if constexpr (F16) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[cur][j] = bf16x8_to_f16x8(fb[cur][j]);
+        }
 #pragma unroll
         for (int q = 0; q < NA; ++q)
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[cur][q][i], fb[cur][j], acc[i][j]);
+            for (int j = 0; j < TN; ++j) acc[i][j] = mma(fa[cur][q][i], fb[cur][j], acc[i][j]);
         if (ks < 3) {
           // Interleave: one fragment read, then a share of the MFMAs.
 #pragma unroll
@@ -268,6 +287,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       hook();
       __builtin_amdgcn_sched_barrier(0);
+      // fp16 mode: the weight fragments of sub-step 0 are converted after the global
+      // loads are issued; those of sub-step ks + 1 inside sub-step ks's MFMA stream, a few
+      // MFMAs after their LDS reads (the weight fragments are read last, two per MFMA), so
+      // the conversion overlaps the matrix core instead of preceding it.
+      constexpr int CONV_AT = (NFRAG - 1) / 2 + 3 < NMFMA ? (NFRAG - 1) / 2 + 3 : NMFMA - 1;
+      if constexpr (F16) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[0][j] = bf16x8_to_f16x8(fb[0][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int cur = ks & 1;
@@ -283,7 +312,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
                 for (int r = 0; r < 2; ++r)
                   if (2 * m + r < NFRAG) read_frag(cur ^ 1, ks + 1, 2 * m + r);
               }
-              acc[i][j] = mfma32x32x16(fa[cur][q][i], fb[cur][j], acc[i][j]);
+              acc[i][j] = mma(fa[cur][q][i], fb[cur][j], acc[i][j]);
+              if constexpr (F16) {
+                if (ks < 3 && m == CONV_AT) {
+#pragma unroll
+                  for (int jj = 0; jj < TN; ++jj) fb[cur ^ 1][jj] = bf16x8_to_f16x8(fb[cur ^ 1][jj]);
+                }
+              }
               __builtin_amdgcn_sched_barrier(0);
             }
         if (ks < 3) {
@@ -332,7 +367,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
           float* row = g.part + ((size_t)slice * g.M + m) * (size_t)(2 * g.N);
           row[(fr < 16 ? 0 : g.N) + f] = v;
         } else if (fr < 16) {
-          put_h(g.out, g.M, g.ldh, m, f, silu_mul(v, other), g.h_planes);
+          put_h(g.out, g.M, g.ldh, m, f, silu_mul(v, other), g.h_fmt);
         }
         continue;
       }
@@ -348,7 +383,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
             row[f] = gate;
             row[g.N + f] = up;
           } else {
-            put_h(g.out, g.M, g.ldh, m, f, silu_mul(gate, up), g.h_planes);
+            put_h(g.out, g.M, g.ldh, m, f, silu_mul(gate, up), g.h_fmt);
           }
         }
       } else {
@@ -392,7 +427,7 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
     SMLP_GEMM_HILO_CONFIGS(SMLP_G)
   } else {
     SMLP_GEMM_CONFIGS(SMLP_G)
-    if constexpr (MODE == GM_DOWN_BF16) {
+    if constexpr (MODE == GM_DOWN_BF16 || MODE == GM_DOWN_F16) {
       SMLP_GEMM_DN_CONFIGS(SMLP_G)
     }
   }
@@ -435,12 +470,12 @@ int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, voi
   a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = 0;
-  a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
+  a.h_fmt = h_format(p.h_dtype);
   a.ldh = a.N;
   if (p.gu_split) {
     // Features [0, gu_split) with the main tile, then the rest with the tail tile: each
     // launch sees its own gate rows (its up rows up_off further on) and h columns.
-    if (a.h_planes != 1 || p.ggu.ksplit != 1 || p.ggu_tail.ksplit != 1) return (int)hipErrorInvalidConfiguration;
+    if (a.h_fmt == 2 || p.ggu.ksplit != 1 || p.ggu_tail.ksplit != 1) return (int)hipErrorInvalidConfiguration;
     a.N = (int)p.gu_split;
     int rc = launch_mode<GM_GATE_UP>(p.ggu, a, s);
     if (rc) return rc;
@@ -456,7 +491,7 @@ int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, voi
   }
   int rc = launch_mode<GM_GATE_UP>(p.ggu, a, s);
   if (rc || p.ggu.ksplit == 1) return rc;
-  return launch_finalize(true, a.part, p.ggu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);
+  return launch_finalize(true, a.part, p.ggu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_fmt, s);
 }
 
 int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {
@@ -478,7 +513,11 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
   a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = p.partial_fp32 ? 1 : 0;
-  a.h_planes = 1;
+  a.h_fmt = h_format(p.h_dtype);
+  // one plane of h: fp16 (the weights converted in registers) or bf16
+  auto one_plane = [&](const GemmPlan& gp, const GArgs& args) {
+    return p.h_dtype == SMLP_FP16 ? launch_mode<GM_DOWN_F16>(gp, args, s) : launch_mode<GM_DOWN_BF16>(gp, args, s);
+  };
   if (p.dn_split) {
     // Columns [0, dn_split) with the main tile, then the rest with the tail tile: each
     // launch sees its own weight rows and output columns (row stride H).  Planned for
@@ -488,7 +527,7 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
     a.N = (int)p.dn_split;
     a.b_rows = a.N;
     a.ldo = (int)p.H;
-    int rc = launch_mode<GM_DOWN_BF16>(p.gdn, a, s);
+    int rc = one_plane(p.gdn, a);
     if (rc) return rc;
     GArgs t = a;
     t.b = a.b + (size_t)p.dn_split * p.ldwd;
@@ -498,10 +537,9 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
     t.tiles_n = p.gdn_tail.tiles / p.gdn_tail.tiles_m;
     t.kslice = p.gdn_tail.kslice;
     t.out = static_cast<char*>(out) + (size_t)p.dn_split * (a.out_f32 ? 4 : 2);
-    return launch_mode<GM_DOWN_BF16>(p.gdn_tail, t, s);
+    return one_plane(p.gdn_tail, t);
   }
-  int rc = p.h_dtype == SMLP_BF16_HILO ? launch_mode<GM_DOWN_HILO>(p.gdn, a, s)
-                                      : launch_mode<GM_DOWN_BF16>(p.gdn, a, s);
+  int rc = p.h_dtype == SMLP_BF16_HILO ? launch_mode<GM_DOWN_HILO>(p.gdn, a, s) : one_plane(p.gdn, a);
   if (rc || p.gdn.ksplit == 1) return rc;
   return launch_finalize(false, a.part, p.gdn.ksplit, a.M, a.N, out, a.N, a.out_f32, 1, s);
 }
@@ -526,7 +564,7 @@ int launch_gemm_linear(const GemmPlan& gp, const void* x, const void* w, void* y
   a.ldo = ldy;
   a.part = part;
   a.out_f32 = out_f32;
-  a.h_planes = 1;
+  a.h_fmt = 1;
   int rc = launch_mode<GM_DOWN_BF16>(gp, a, s);
   if (rc || gp.ksplit == 1) return rc;
   return launch_finalize(false, part, gp.ksplit, M, N, y, ldy, out_f32, 1, s);

@@ -40,7 +40,7 @@ struct Plan {
   int64_t M, H, I;
   int dtype;
   int partial_fp32;
-  int h_dtype;              // SMLP_FP32, SMLP_BF16 or SMLP_BF16_HILO
+  int h_dtype;              // SMLP_FP32, SMLP_BF16, SMLP_BF16_HILO or SMLP_FP16
   size_t h_offset, h_bytes;
   size_t part_offset, part_bytes;   // split-K partial sums
   size_t workspace_bytes;
@@ -64,9 +64,10 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
 
 // Sum K-split partials [ksplit][M][P*N] in slice order and apply the stage epilogue
-// (gate_up: SiLU-and-mul into h with `h_planes` bf16 planes; down: bf16 or fp32 out).
+// (gate_up: SiLU-and-mul into h, h_fmt 1 = one bf16 plane, 2 = bf16 hi + lo, 3 = fp16;
+// down: bf16 or fp32 out).
 int launch_finalize(bool gate_up, const float* part, int ksplit, int M, int N, void* out,
-                    int ldo, int out_f32, int h_planes, hipStream_t s);
+                    int ldo, int out_f32, int h_fmt, hipStream_t s);
 
 // Plain projection y = x . w^T (bf16 operands; y bf16 or fp32 with row stride ldy):
 // the streaming kernel (plan kind SKINNY_STREAM16, M <= 32) or the LDS-tiled kernel,

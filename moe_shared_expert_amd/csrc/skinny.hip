@@ -495,7 +495,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_direct_kernel(SkArgs a) {
 template <bool GU>
 __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__ part,
                                                        int ksplit, int M, int N, void* out,
-                                                       int ldo, int out_f32, int h_planes) {
+                                                       int ldo, int out_f32, int h_fmt) {
   // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, up to
   // sixteen slices in flight at a time, summed in slice order.  Down and projection outputs
   // have row stride ldo (a multiple of 4).
@@ -530,16 +530,21 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
     }
     const size_t o = (size_t)m * (GU ? N : ldo) + n;
     if (GU) {
+      // h as one bf16 plane (h_fmt 1), bf16 hi + lo planes (2) or one fp16 plane (3)
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float h = silu_mul(g[j], u[j]);
-        hi[j] = f2bf(h);
-        lo[j] = f2bf(h - __uint_as_float(hi[j] << 16));
+        if (h_fmt == 3) {
+          hi[j] = f2h(h);
+        } else {
+          hi[j] = f2bf(h);
+          lo[j] = f2bf(h - __uint_as_float(hi[j] << 16));
+        }
       }
       uint16_t* hp = reinterpret_cast<uint16_t*>(out);
       *reinterpret_cast<u32x2*>(hp + o) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-      if (h_planes == 2)
+      if (h_fmt == 2)
         *reinterpret_cast<u32x2*>(hp + (size_t)M * N + o) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     } else if (out_f32) {
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = g;
@@ -618,7 +623,7 @@ static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
 }
 
 int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* out, int ldo,
-                    int out_f32, int h_planes, hipStream_t s) {
+                    int out_f32, int h_fmt, hipStream_t s) {
   if (N % 4 != 0 || ldo % 4 != 0) return (int)hipErrorInvalidValue;
   const size_t total = (size_t)M * (N / 4);
   // Small outputs (a decode step's partials) take 64-thread workgroups so that every
@@ -628,10 +633,10 @@ int launch_finalize(bool gu, const float* part, int ksplit, int M, int N, void* 
   if (blocks > (size_t)2048 * 256 / threads) blocks = (size_t)2048 * 256 / threads;
   if (gu)
     hipLaunchKernelGGL(skinny_finalize<true>, dim3((unsigned)blocks), dim3(threads), 0, s, part, ksplit, M,
-                       N, out, ldo, out_f32, h_planes);
+                       N, out, ldo, out_f32, h_fmt);
   else
     hipLaunchKernelGGL(skinny_finalize<false>, dim3((unsigned)blocks), dim3(threads), 0, s, part, ksplit,
-                       M, N, out, ldo, out_f32, h_planes);
+                       M, N, out, ldo, out_f32, h_fmt);
   return (int)hipGetLastError();
 }
 

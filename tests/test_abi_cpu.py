@@ -212,9 +212,19 @@ def test_workspace_and_plan(L):
             binding.shared_mlp_tune_h_planes(3)
     finally:
         binding.shared_mlp_tune_h_planes(0)
-    p = binding.shared_mlp_plan(8192, H, I)
-    assert p["path_name"] == "large_m" and p["h_dtype"] == BF16
+    p = binding.shared_mlp_plan(8192, H, I)   # bf16 output: h as one fp16 plane
+    assert p["path_name"] == "large_m" and p["h_dtype"] == binding.SMLP_FP16
     assert p["workspace_bytes"] >= 8192 * I * 2
+    # an fp32 partial keeps one bf16 plane; the tuning hook pins any format
+    assert binding.shared_mlp_plan(8192, H, I, BF16, True)["h_dtype"] == BF16
+    try:
+        for fmt, want in ((1, BF16), (2, binding.SMLP_BF16_HILO), (3, binding.SMLP_FP16)):
+            binding.shared_mlp_tune_h_format(fmt)
+            assert binding.shared_mlp_plan(512, H, I)["h_dtype"] == want
+        with pytest.raises(binding.SmlpError):
+            binding.shared_mlp_tune_h_format(4)
+    finally:
+        binding.shared_mlp_tune_h_format(0)
     p = binding.shared_mlp_plan(12, 16, 12, FP32)
     assert p["path_name"] == "fp32"
     p = binding.shared_mlp_plan(0, H, I)

@@ -403,8 +403,11 @@ DOWN_TILES = GATE_UP_TILES + [(128, 32, 4, 1, 2), (128, 32, 4, 1, 4)]
 
 
 @pytest.mark.parametrize("ksplit", [1, 3])
-@pytest.mark.parametrize("stage,tile", [(0, t) for t in GATE_UP_TILES] + [(1, t) for t in DOWN_TILES])
-def test_every_compiled_tile(stage, tile, ksplit):
+@pytest.mark.parametrize("stage,tile,partial", [(0, t, True) for t in GATE_UP_TILES] +
+                         [(1, t, p) for t in DOWN_TILES for p in (True, False)])
+def test_every_compiled_tile(stage, tile, partial, ksplit):
+    # the down tiles run with an fp32 partial (h as one bf16 plane) and with a bf16 output
+    # (h as one fp16 plane, the weight fragments converted in registers)
     M, Hh, Ii = 300, 1032, 392
     x = synth.activations(M, Hh, config=12, copy=1)
     wgu, wd = synth.layer_weights(Hh, Ii, config=12)
@@ -412,14 +415,15 @@ def test_every_compiled_tile(stage, tile, ksplit):
     prev = binding.shared_mlp_set_large_m_threshold(1)
     try:
         binding.shared_mlp_tune_gemm(stage, *tile, ksplit=ksplit)
-        p = binding.shared_mlp_plan(M, Hh, Ii, binding.SMLP_BF16, True)
+        p = binding.shared_mlp_plan(M, Hh, Ii, binding.SMLP_BF16, partial)
         assert p["path_name"] == "large_m"
+        assert p["h_dtype"] == (binding.SMLP_BF16 if partial else binding.SMLP_FP16)
         assert (p["gate_up_ksplit"] if stage == 0 else p["down_ksplit"]) == ksplit
-        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=True)
+        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=partial)
     finally:
         binding.shared_mlp_tune_gemm(stage)
         binding.shared_mlp_set_large_m_threshold(prev)
-    assert_rms_close(out, ref, BF16_TOL, f"stage {stage} tile {tile} ksplit {ksplit}")
+    assert_rms_close(out, ref, BF16_TOL, f"stage {stage} tile {tile} ksplit {ksplit} partial {partial}")
 
 
 def test_m_zero_leaves_output_untouched():
