@@ -10,6 +10,7 @@
 #include <string>
 
 #include "internal.h"
+#include "tile_configs.h"
 #include "smlp.h"
 #include "smlp_latent.h"
 #include "smlp_tuning.h"

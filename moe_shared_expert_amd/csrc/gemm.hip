@@ -33,6 +33,7 @@
 #include "device_common.h"
 #include "internal.h"
 #include "smlp.h"
+#include "tile_configs.h"
 
 namespace smlp {
 
@@ -403,18 +404,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
     }
 }
 
-// Tile configurations (BM, BN, WM, WN, stages).  LDS holds stages x (BM + BN) x 128
-// bytes (the two-plane down mode: stages x (2 BM + BN) x 128) of the 160 KB per
-// workgroup.
-#define SMLP_GEMM_CONFIGS(X)                                                                    \
-  X(256, 256, 2, 4, 2) X(128, 256, 2, 4, 3) X(128, 256, 2, 2, 3) X(128, 128, 2, 2, 2)           \
-  X(128, 128, 2, 2, 4) X(128, 128, 4, 2, 4) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4) X(128, 64, 4, 1, 6) \
-  X(128, 128, 4, 2, 2) X(128, 128, 4, 2, 3) X(128, 256, 2, 4, 2) X(256, 128, 4, 2, 2) X(256, 128, 4, 2, 3) \
-  X(128, 64, 4, 2, 3) X(128, 64, 4, 2, 4) X(64, 64, 2, 2, 4)
-// Down only (one MFMA tile column per wave cannot pair gate and up rows).
-#define SMLP_GEMM_DN_CONFIGS(X) X(128, 32, 4, 1, 2) X(128, 32, 4, 1, 4)
-#define SMLP_GEMM_HILO_CONFIGS(X) X(128, 128, 2, 2, 3) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4)
-
 template <int MODE>
 int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
   const dim3 grid(gp.tiles, gp.ksplit);
@@ -436,21 +425,6 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns) {
-#define SMLP_GM(BM_, BN_, WM_, WN_, NS_) \
-  if (bm == BM_ && bn == BN_ && wm == WM_ && wn == WN_ && ns == NS_) return true;
-  if (stage == 1 && hilo) {
-    SMLP_GEMM_HILO_CONFIGS(SMLP_GM)
-  } else {
-    SMLP_GEMM_CONFIGS(SMLP_GM)
-    if (stage == 1) {
-      SMLP_GEMM_DN_CONFIGS(SMLP_GM)
-    }
-  }
-#undef SMLP_GM
-  return false;
-}
 
 int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s) {
   GArgs a{};

@@ -58,7 +58,6 @@ struct Plan {
 };
 
 // Weight-streaming stages (skinny.hip).  Return a hipError_t.
-bool skinny_instantiated(int stage, int kind, int mt, int nb, int waves, int u);  // stage 0 gate_up, 1 down, 2 projection
 int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
                           hipStream_t s);
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
@@ -82,7 +81,6 @@ int launch_restore_logical(const void* src, void* dst, int64_t M, int64_t N, con
                            int nr, int tp, int elem_bytes, hipStream_t s);
 
 // LDS-tiled GEMM stages (gemm.hip).
-bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns);  // stage 0: gate_up, 1: down
 int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s);
 int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
 

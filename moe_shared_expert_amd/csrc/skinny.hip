@@ -32,6 +32,7 @@
 #include "device_common.h"
 #include "internal.h"
 #include "smlp.h"
+#include "tile_configs.h"
 
 namespace smlp {
 
@@ -553,42 +554,6 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
           u32x2{f2bf(g[0]) | (f2bf(g[1]) << 16), f2bf(g[2]) | (f2bf(g[3]) << 16)};
     }
   }
-}
-
-// Instantiated configurations (MT, NB, WAVES, U) per kernel kind (MT = 16-token
-// tiles; none spills registers).  Streaming kind: NB = 16-row MFMA tiles, U = ring
-// stages, LDS = WAVES x STAGES x (NB + activation tiles) x 2 KB <= 160 KB with
-// activation tiles = MT (gate_up) or 2 MT (down).  Direct kind: NB = 16-feature
-// blocks, U = 64-element K steps per wave per pipeline stage.
-#define SMLP_SK_GU_STREAM16(X)                                                                 \
-  X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 2, 4, 4) X(1, 2, 8, 3) X(1, 3, 4, 3) X(1, 3, 4, 4)          \
-  X(1, 3, 4, 5) X(1, 3, 8, 2) X(1, 4, 4, 4) X(2, 1, 4, 4) X(2, 2, 4, 4) X(2, 3, 4, 3)          \
-  X(2, 3, 4, 4) X(2, 4, 4, 3)
-#define SMLP_SK_DN_STREAM16(X)                                                                 \
-  X(1, 1, 4, 4) X(1, 1, 8, 3) X(1, 2, 4, 3) X(1, 2, 4, 4) X(1, 2, 4, 5) X(1, 2, 8, 2)          \
-  X(1, 3, 4, 4) X(1, 4, 4, 3) X(2, 1, 4, 4) X(2, 2, 4, 3) X(2, 3, 4, 2) X(2, 4, 4, 2)
-// Projection (one activation plane): deeper rings, so that a wave keeps more weight
-// bytes in flight when a workgroup holds only one or two 16-row tiles.
-#define SMLP_SK_LIN_STREAM16(X)                                                                \
-  X(1, 1, 4, 4) X(1, 1, 4, 6) X(1, 1, 4, 8) X(1, 1, 8, 3) X(1, 1, 8, 4) X(1, 1, 8, 5)          \
-  X(1, 2, 4, 4) X(1, 2, 4, 6) X(1, 2, 8, 3) X(1, 3, 4, 4) X(1, 4, 4, 4) X(2, 1, 4, 4)          \
-  X(2, 1, 4, 6) X(2, 1, 8, 3) X(2, 2, 4, 4) X(2, 2, 8, 2)
-#define SMLP_SK_GU_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1) X(8, 1, 8, 1)
-#define SMLP_SK_DN_DIRECT16(X) X(4, 1, 4, 1) X(4, 1, 8, 1) X(8, 1, 4, 1)
-bool skinny_instantiated(int stage, int kind, int mt, int nb, int waves, int u) {
-#define SMLP_MATCH(MT_, NB_, W_, U_) \
-  if (mt == MT_ && nb == NB_ && waves == W_ && u == U_) return true;
-  if (stage == 2) {
-    if (kind == SKINNY_STREAM16) { SMLP_SK_LIN_STREAM16(SMLP_MATCH) }
-  } else if (stage == 0) {
-    if (kind == SKINNY_DIRECT16) { SMLP_SK_GU_DIRECT16(SMLP_MATCH) }
-    if (kind == SKINNY_STREAM16) { SMLP_SK_GU_STREAM16(SMLP_MATCH) }
-  } else {
-    if (kind == SKINNY_DIRECT16) { SMLP_SK_DN_DIRECT16(SMLP_MATCH) }
-    if (kind == SKINNY_STREAM16) { SMLP_SK_DN_STREAM16(SMLP_MATCH) }
-  }
-#undef SMLP_MATCH
-  return false;
 }
 
 template <int MODE>
