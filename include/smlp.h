@@ -118,6 +118,23 @@ int shared_mlp_forward(const void* x, const void* w_gate_up, const void* w_down,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * shared_mlp_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The intermediate h and any K-split
+ * partial sums live in a static device array of SMLP_NOALLOC_SCRATCH_BYTES bytes
+ * (32 MiB), one per GPU, held from library load until the process ends.  A call whose
+ * plan needs more (shared_mlp_plan's workspace_bytes; e.g. the M = 8192 prefill) returns
+ * SMLP_ERR_WORKSPACE before any HIP call.  Every call on one GPU uses that GPU's array:
+ * calls that overlap on one GPU (concurrent streams or threads) race and must be
+ * serialised by the caller.  The array keeps the last call's contents; nothing in it
+ * needs to start at zero.  Arguments and results are those of shared_mlp_forward.
+ */
+#define SMLP_NOALLOC_SCRATCH_BYTES (32u << 20)
+int shared_mlp_forward_noalloc(const void* x, const void* w_gate_up, const void* w_down, void* out,
+                               int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32,
+                               hipStream_t stream);
+
+/*
  * The two halves of shared_mlp_forward, for callers that time or test them apart.
  * shared_mlp_gate_up_act computes h = SiLU(x Wg^T) * (x Wu^T) into the workspace
  * (at smlp_plan.h_offset, as smlp_plan.h_dtype); shared_mlp_down then computes out

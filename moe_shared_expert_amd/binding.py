@@ -48,6 +48,7 @@ EXPORTS = {
     "shared_mlp_plan": (_int, [_i64, _i64, _i64, _int, _int, ctypes.POINTER(_Plan)]),
     "shared_mlp_workspace_bytes": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
     "shared_mlp_forward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "shared_mlp_forward_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp]),
     "shared_mlp_gate_up_act": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "shared_mlp_down": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "shared_mlp_set_large_m_threshold": (_i64, [_i64]),
@@ -213,6 +214,17 @@ def shared_mlp_forward(x, w_gate_up, w_down, out, partial_fp32=False, workspace=
     _check(lib().shared_mlp_forward(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), M, H, I, dt,
                                     int(bool(partial_fp32)), _ptr(workspace), _ws_bytes(workspace),
                                     _stream(stream, x.device)))
+    return out
+
+
+def shared_mlp_forward_noalloc(x, w_gate_up, w_down, out, partial_fp32=False, stream=None):
+    """shared_mlp_forward on the library's static per-GPU scratch array: no workspace and
+    no allocation (calls that overlap on one GPU race; see include/smlp.h)."""
+    M, H, I = _shapes(x, w_gate_up, w_down, out)
+    _check_types(x, (("w_gate_up", w_gate_up), ("w_down", w_down)), out, partial_fp32)
+    dt = _dtype_code(x)
+    _check(lib().shared_mlp_forward_noalloc(_ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(out), M, H, I, dt,
+                                            int(bool(partial_fp32)), _stream(stream, x.device)))
     return out
 
 

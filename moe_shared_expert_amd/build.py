@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsmlp.so")
 
-SOURCES = ["api.cpp", "layout.cpp", "skinny.hip", "gemm.hip", "aux.hip", "latent.hip", "ceilings.hip"]
+SOURCES = ["api.cpp", "layout.cpp", "skinny.hip", "gemm.hip", "aux.hip", "latent.hip", "ceilings.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

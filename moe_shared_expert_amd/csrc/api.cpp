@@ -770,6 +770,30 @@ int shared_mlp_forward(const void* x, const void* w_gate_up, const void* w_down,
              workspace_bytes, stream);
 }
 
+int shared_mlp_forward_noalloc(const void* x, const void* w_gate_up, const void* w_down, void* out,
+                               int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32,
+                               hipStream_t stream) {
+  // Host-side checks first (no HIP call before them): the plan, the scratch limit and
+  // the pointers; run() repeats the full validation against the scratch array.
+  smlp::Plan p;
+  int rc = make_plan(M, H, I, dtype, partial_fp32, &p);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if (p.workspace_bytes > (size_t)SMLP_NOALLOC_SCRATCH_BYTES)
+    return fail(SMLP_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch, more than the %zu bytes of the static scratch array "
+                "(call shared_mlp_forward with a workspace instead)",
+                p.workspace_bytes, (size_t)SMLP_NOALLOC_SCRATCH_BYTES);
+  const size_t al = dtype == SMLP_BF16 ? 16 : 4;
+  if ((rc = check_ptr(x, "x", al)) || (rc = check_ptr(w_gate_up, "w_gate_up", al)) ||
+      (rc = check_ptr(w_down, "w_down", al)) || (rc = check_ptr(out, "out", al)))
+    return rc;
+  void* scratch = nullptr;
+  if ((rc = hip_status(smlp::noalloc_scratch(&scratch), "static scratch lookup"))) return rc;
+  return run(kBoth, x, w_gate_up, w_down, out, M, H, I, dtype, partial_fp32, scratch,
+             (size_t)SMLP_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int shared_mlp_gate_up_act(const void* x, const void* w_gate_up, int64_t M, int64_t H,
                            int64_t I, int dtype, int partial_fp32, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {

@@ -84,6 +84,10 @@ int launch_restore_logical(const void* src, void* dst, int64_t M, int64_t N, con
 int launch_gemm_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws, hipStream_t s);
 int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
 
+// Device address of this device's static scratch array (noalloc.hip), looked up with
+// hipGetSymbolAddress on the first call per device and cached.  Returns a hipError_t.
+int noalloc_scratch(void** ptr);
+
 // fp32 stages and helpers (aux.hip).
 int launch_fp32_gate_up(const Plan& p, const float* x, const float* w_gate_up, void* ws,
                         hipStream_t s);

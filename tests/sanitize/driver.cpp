@@ -88,6 +88,17 @@ static void forward_validation() {
   for (int s = -1; s <= 9; ++s) EXPECT(shared_mlp_status_string(s) != nullptr);
 }
 
+static void noalloc_validation() {
+  void *x = fake(1ull << 40), *wgu = fake(2ull << 40), *wd = fake(3ull << 40), *out = fake(4ull << 40);
+  // the M = 8192 prefill needs more than the static scratch: refused before any HIP call
+  EXPECT(shared_mlp_forward_noalloc(x, wgu, wd, out, 8192, 7168, 6144, SMLP_BF16, 0, nullptr) == SMLP_ERR_WORKSPACE);
+  EXPECT(shared_mlp_forward_noalloc(nullptr, wgu, wd, out, 16, 7168, 6144, SMLP_BF16, 0, nullptr) == SMLP_ERR_NULL);
+  EXPECT(shared_mlp_forward_noalloc(x, wgu, wd, out, 16, 7168, 6143, SMLP_BF16, 0, nullptr) == SMLP_ERR_SHAPE);
+  EXPECT(shared_mlp_forward_noalloc(x, wgu, wd, out, 0, 7168, 6144, SMLP_BF16, 0, nullptr) == SMLP_OK);
+  // valid arguments reach the scratch lookup (a stand-in here, which fails)
+  EXPECT(shared_mlp_forward_noalloc(x, wgu, wd, out, 16, 7168, 6144, SMLP_BF16, 0, nullptr) == SMLP_ERR_HIP);
+}
+
 static void latent_validation() {
   void *x = fake(1ull << 40), *w = fake(2ull << 40), *y = fake(3ull << 40), *ws = fake(4ull << 40);
   size_t need = 0;
@@ -162,6 +173,7 @@ static void threads() {
 int main() {
   plans();
   forward_validation();
+  noalloc_validation();
   latent_validation();
   layout_models();
   tuning();
