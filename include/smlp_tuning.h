@@ -47,6 +47,21 @@ int shared_mlp_tune_h_planes(int planes);
  * SMLP_ERR_ARG. */
 int shared_mlp_tune_h_format(int fmt);
 
+/* Gate_up stage of the tiled path (33 <= M <= 256) as the weight-streaming kernel split
+ * over 16- or 32-token tiles, full K per workgroup, SiLU-and-mul fused (no K-split
+ * partials): 0 = automatic, 1 = wherever it applies (at most 4 MFMA tiles of features per
+ * workgroup), 2 = never.  The small-M overrides of stage 0 (nb, waves, u) apply to it.
+ * Process-wide, for subsequent plans.  Returns SMLP_OK or SMLP_ERR_ARG. */
+int shared_mlp_tune_token_split(int mode);
+
+/* Token count from which a tiled down stage that reads fp16 h converts w_down to an fp16
+ * copy in the workspace once (one streaming pass, counted in the workspace size and the
+ * kernel count) instead of converting its weight fragments in registers (default 1024;
+ * 1 = always, a value above any M = never).  Results are identical either way (the
+ * conversion is exact).  Returns the previous value, or -1 (SMLP_ERR_ARG) if min_m < 1.
+ * Process-wide, for subsequent plans. */
+int64_t shared_mlp_tune_weight_convert(int64_t min_m);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,8 @@ TUNING_EXPORTS = {
     "shared_mlp_tune_gemm": (_int, [_int, _int, _int, _int, _int, _int, _int]),
     "shared_mlp_tune_h_planes": (_int, [_int]),
     "shared_mlp_tune_h_format": (_int, [_int]),
+    "shared_mlp_tune_weight_convert": (_i64, [_i64]),
+    "shared_mlp_tune_token_split": (_int, [_int]),
 }
 
 
@@ -281,6 +283,19 @@ def shared_mlp_tune_gemm(stage: int, bm: int = 0, bn: int = 0, wm: int = 0, wn: 
 def shared_mlp_tune_h_planes(planes: int = 0):
     """Planes of h on the small-M path (0 = automatic); see include/smlp_tuning.h."""
     _check(lib().shared_mlp_tune_h_planes(planes))
+
+
+def shared_mlp_tune_token_split(mode: int = 0):
+    """Token-split gate_up on the tiled path (0 auto, 1 always, 2 never); see include/smlp_tuning.h."""
+    _check(lib().shared_mlp_tune_token_split(mode))
+
+
+def shared_mlp_tune_weight_convert(min_m: int) -> int:
+    """Token count from which the fp16-h down stage converts w_down once; returns the previous value."""
+    prev = lib().shared_mlp_tune_weight_convert(int(min_m))
+    if prev < 0:
+        _check(8)
+    return prev
 
 
 def shared_mlp_tune_h_format(fmt: int = 0):

@@ -81,6 +81,14 @@ GemmOverride g_gtune[3];
 std::atomic<int> g_h_planes{0};
 // Format of h on the large-M path (0 = automatic), see shared_mlp_tune_h_format.
 std::atomic<int> g_h_format{0};
+// Token-split gate_up on the tiled path (0 = automatic, 1 = always where it applies,
+// 2 = never), see shared_mlp_tune_token_split.
+std::atomic<int> g_tsplit{0};
+
+// Token count from which a large-M down stage with fp16 h converts w_down to fp16 once
+// (into the workspace) instead of converting its weight fragments in registers, see
+// shared_mlp_tune_weight_convert.
+std::atomic<int64_t> g_wd16_min_m{1024};
 
 // Small-M stage plan.  M <= 32: the streaming kernel, one workgroup per compute unit
 // over an equal contiguous share of the features (gate_up) or rows (down), the whole K
@@ -213,6 +221,60 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     sp.fpw = 0;
   }
   if (!smlp::skinny_instantiated(inst, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
+  *out = sp;
+  return true;
+}
+
+// Default choice of the token-split gate_up (measured on MI355X, H = 7168): off until
+// measured.
+bool token_split_default(int64_t M, int64_t N) {
+  (void)M;
+  (void)N;
+  return false;
+}
+
+// Token-split gate_up for the tiled path: the weight-streaming kernel over tiles of 16 * mt
+// tokens (ttiles workgroups along M) and nt 16-row tiles of 8 features each (along I),
+// the full K range per workgroup, so the gate and up sums of a feature never leave
+// registers and SiLU-and-mul is the kernel's epilogue (no K-split partials, no finalize
+// launch).  The workgroups of one feature range share its weights through their XCD's L2.
+// Sized to about one workgroup per compute unit; applies while every workgroup holds at
+// most 4 tiles (N up to ~1024 features at M = 128).  Returns false when it does not apply.
+bool plan_token_split(int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* out) {
+  using namespace smlp;
+  const SkinnyOverride& o = g_tune[0];
+  SkinnyPlan sp{};
+  sp.kind = SKINNY_STREAM16;
+  sp.mt = M > 128 ? 2 : 1;
+  const int64_t tok = 16 * sp.mt;
+  const int64_t tt = (M + tok - 1) / tok;
+  int64_t groups = (kCUs + tt / 2) / tt;
+  if (groups < 1) groups = 1;
+  int64_t fpw = (N + groups - 1) / groups;
+  fpw = (fpw + 7) / 8 * 8;
+  int64_t nt = o.nb.load() ? o.nb.load() : fpw / 8;
+  if (nt < 1 || nt > 4) return false;
+  fpw = 8 * nt;
+  groups = (N + fpw - 1) / fpw;
+  // measured preferences for the (waves, stages) of the ring, else any compiled pair
+  static const int kPref[][2] = {{4, 4}, {4, 3}, {8, 2}, {8, 3}, {8, 4}, {4, 5}};
+  sp.nb = (int)nt;
+  sp.waves = o.waves.load();
+  sp.u = o.u.load();
+  for (const auto& c : kPref) {
+    const int w = sp.waves ? sp.waves : c[0], st = sp.u ? sp.u : c[1];
+    if (skinny_instantiated(0, sp.kind, sp.mt, sp.nb, w, st)) {
+      sp.waves = w;
+      sp.u = st;
+      break;
+    }
+  }
+  if (!sp.waves || !sp.u || !skinny_instantiated(0, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
+  sp.fpw = (int)fpw;
+  sp.ksplit = 1;
+  sp.kslice = (int)((K + 63) / 64 * 64);
+  sp.ttiles = (int)tt;
+  sp.blocks = (int)(groups * tt);
   *out = sp;
   return true;
 }
@@ -512,20 +574,31 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     // Only the down stage reads h; its two-plane form has its own tile list.
     if (!plan_gemm(0, M, I, H, false, &p->ggu) || !plan_gemm(1, M, H, I, hilo, &p->gdn))
       return fail(SMLP_ERR_ARG, "the pinned large-M tile is not a compiled configuration");
+    const int ts = g_tsplit.load();
+    if (ts != 2 && M <= 256 && (ts == 1 || token_split_default(M, I)) && plan_token_split(M, I, H, &p->gu))
+      p->gu_tsplit = 1;
     size_t part = 0;
-    if (p->ggu.ksplit > 1) part = (size_t)p->ggu.ksplit * M * 2 * I * 4;
+    if (!p->gu_tsplit && p->ggu.ksplit > 1) part = (size_t)p->ggu.ksplit * M * 2 * I * 4;
     if (p->gdn.ksplit > 1) {
       const size_t d = (size_t)p->gdn.ksplit * M * H * 4;
       if (d > part) part = d;
     }
     p->part_bytes = round_up(part, 256);
-    p->kernels = 2 + (p->ggu.ksplit > 1) + (p->gdn.ksplit > 1);
+    p->kernels = 2 + (!p->gu_tsplit && p->ggu.ksplit > 1) + (p->gdn.ksplit > 1);
     if (split_columns(1, M, H, I, &p->gdn, &p->gdn_tail, &p->dn_split)) p->kernels += 1;
-    if (!hilo && split_columns(0, M, I, H, &p->ggu, &p->ggu_tail, &p->gu_split)) p->kernels += 1;
+    if (!hilo && !p->gu_tsplit && split_columns(0, M, I, H, &p->ggu, &p->ggu_tail, &p->gu_split)) p->kernels += 1;
+    // With fp16 h and many tokens, converting each weight fragment in registers costs more
+    // than one streaming pass over w_down (M = 2048: +72 us in registers against ~27 us for
+    // the pass; M = 8192: +130 us): convert once into the workspace.
+    if (p->h_dtype == SMLP_FP16 && M >= g_wd16_min_m.load()) {
+      p->wd16_bytes = round_up((size_t)(H * I) * 2, 256);
+      p->kernels += 1;
+    }
   }
   p->h_offset = 0;
   p->part_offset = p->h_bytes;
-  p->workspace_bytes = p->h_bytes + p->part_bytes;
+  p->wd16_offset = p->h_bytes + p->part_bytes;
+  p->workspace_bytes = p->h_bytes + p->part_bytes + p->wd16_bytes;
   p->up_off = I;
   p->ldwd = I;
   return ok();
@@ -676,7 +749,10 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
         rc = smlp::launch_fp32_gate_up(p, (const float*)x, (const float*)wgu, ws, stream);
         break;
       case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_gate_up(p, x, wgu, ws, stream); break;
-      default: rc = smlp::launch_gemm_gate_up(p, x, wgu, ws, stream); break;
+      default:
+        rc = p.gu_tsplit ? smlp::launch_skinny_gate_up(p, x, wgu, ws, stream)
+                         : smlp::launch_gemm_gate_up(p, x, wgu, ws, stream);
+        break;
     }
     if ((rc = hip_status(rc, "gate_up launch"))) return rc;
   }
@@ -738,9 +814,9 @@ int shared_mlp_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32
     plan->gate_up_blocks = p.gu.blocks;
     plan->down_blocks = p.dn.blocks;
   } else if (p.path == SMLP_PATH_LARGE_M) {
-    plan->gate_up_ksplit = p.ggu.ksplit;
+    plan->gate_up_ksplit = p.gu_tsplit ? 1 : p.ggu.ksplit;
     plan->down_ksplit = p.gdn.ksplit;
-    plan->gate_up_blocks = p.ggu.tiles * p.ggu.ksplit + (p.gu_split ? p.ggu_tail.tiles : 0);
+    plan->gate_up_blocks = p.gu_tsplit ? p.gu.blocks : p.ggu.tiles * p.ggu.ksplit + (p.gu_split ? p.ggu_tail.tiles : 0);
     plan->down_blocks = p.gdn.tiles * p.gdn.ksplit + (p.dn_split ? p.gdn_tail.tiles : 0);
   } else {
     plan->gate_up_ksplit = plan->down_ksplit = 1;
@@ -932,7 +1008,10 @@ int shared_mlp_forward_rank(const void* x, const void* w_gate_up, const void* w_
   switch (p.path) {
     case SMLP_PATH_FP32: rc = smlp::launch_fp32_gate_up(p, (const float*)x, (const float*)gu, workspace, stream); break;
     case SMLP_PATH_SMALL_M: rc = smlp::launch_skinny_gate_up(p, x, gu, workspace, stream); break;
-    default: rc = smlp::launch_gemm_gate_up(p, x, gu, workspace, stream); break;
+    default:
+      rc = p.gu_tsplit ? smlp::launch_skinny_gate_up(p, x, gu, workspace, stream)
+                       : smlp::launch_gemm_gate_up(p, x, gu, workspace, stream);
+      break;
   }
   if ((rc = hip_status(rc, "gate_up launch"))) return rc;
   switch (p.path) {
@@ -971,6 +1050,21 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
 int shared_mlp_tune_h_planes(int planes) {
   if (planes < 0 || planes > 2) return fail(SMLP_ERR_ARG, "planes = %d outside {0, 1, 2}", planes);
   g_h_planes = planes;
+  return ok();
+}
+
+int64_t shared_mlp_tune_weight_convert(int64_t min_m) {
+  if (min_m < 1) {
+    fail(SMLP_ERR_ARG, "min_m = %lld < 1", (long long)min_m);
+    return -1;
+  }
+  ok();
+  return g_wd16_min_m.exchange(min_m);
+}
+
+int shared_mlp_tune_token_split(int mode) {
+  if (mode < 0 || mode > 2) return fail(SMLP_ERR_ARG, "mode = %d outside {0, 1, 2}", mode);
+  g_tsplit = mode;
   return ok();
 }
 

@@ -185,3 +185,31 @@ int launch_rms_rescale(const float* in, uint16_t* out, int64_t M, int64_t H, hip
 }
 
 }  // namespace smlp
+
+namespace smlp {
+
+// bf16 -> fp16 copy of a weight matrix (rows x cols, source row stride ld_src elements,
+// destination dense), eight elements per thread; exact for every value in the fp16
+// normal range (see bf16x8_to_f16x8).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                                          int64_t rows, int64_t cols, uint16_t* __restrict__ dst) {
+  const int64_t c8 = cols / 8, total = rows * c8;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / c8, c = (e % c8) * 8;
+    const u32x4 v = ld_stream(src + r * ld_src + c);
+    *reinterpret_cast<u32x4*>(dst + r * cols + c) = bf16x8_to_f16x8(v);
+  }
+}
+
+int launch_bf16_to_f16(const void* src, int64_t ld_src, int64_t rows, int64_t cols, void* dst, hipStream_t s) {
+  if (cols % 8 || ld_src % 8) return (int)hipErrorInvalidValue;
+  const int64_t total = rows * (cols / 8);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint16_t*>(src),
+                     ld_src, rows, cols, static_cast<uint16_t*>(dst));
+  return (int)hipGetLastError();
+}
+
+}  // namespace smlp

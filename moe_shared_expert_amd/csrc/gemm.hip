@@ -40,7 +40,7 @@ namespace smlp {
 namespace {
 
 
-enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2, GM_DOWN_F16 = 3 };
+enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2, GM_DOWN_F16 = 3, GM_DOWN_F16W = 4 };
 
 struct GArgs {
   const uint16_t* a;      // [M, K] bf16 (down, two planes: hi)
@@ -133,7 +133,8 @@ __device__ __forceinline__ void wait_steps(int later) {
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   constexpr bool GU = MODE == GM_GATE_UP;
-  constexpr bool F16 = MODE == GM_DOWN_F16;
+  constexpr bool F16 = MODE == GM_DOWN_F16;      // fp16 h, bf16 weights converted in registers
+  constexpr bool F16W = MODE == GM_DOWN_F16W;    // fp16 h, fp16 weights (converted beforehand)
   constexpr int NA = MODE == GM_DOWN_HILO ? 2 : 1;
   constexpr int W = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   // reads behind, keep the compiler's schedule (measured slightly faster there).
   constexpr bool PINNED = NMFMA >= NFRAG;
   auto mma = [](u32x4 a, u32x4 b, f32x16 c) {
-    if constexpr (F16) return mfma32x32x16_f16(a, b, c);
+    if constexpr (F16 || F16W) return mfma32x32x16_f16(a, b, c);
     else return mfma32x32x16(a, b, c);
   };
   auto compute = [&](int buf, auto&& hook) {
@@ -416,7 +417,7 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
     SMLP_GEMM_HILO_CONFIGS(SMLP_G)
   } else {
     SMLP_GEMM_CONFIGS(SMLP_G)
-    if constexpr (MODE == GM_DOWN_BF16 || MODE == GM_DOWN_F16) {
+    if constexpr (MODE == GM_DOWN_BF16 || MODE == GM_DOWN_F16 || MODE == GM_DOWN_F16W) {
       SMLP_GEMM_DN_CONFIGS(SMLP_G)
     }
   }
@@ -488,9 +489,17 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = p.partial_fp32 ? 1 : 0;
   a.h_fmt = h_format(p.h_dtype);
-  // one plane of h: fp16 (the weights converted in registers) or bf16
+  if (p.wd16_bytes) {
+    // fp16 h against an fp16 copy of the weights, converted once before the GEMM
+    int rc = launch_bf16_to_f16(w_down, p.ldwd, p.H, p.I, static_cast<char*>(ws) + p.wd16_offset, s);
+    if (rc) return rc;
+    a.b = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.wd16_offset);
+    a.ldb = (int)p.I;
+  }
+  // one plane of h: fp16 (weights fp16 already, or converted in registers) or bf16
   auto one_plane = [&](const GemmPlan& gp, const GArgs& args) {
-    return p.h_dtype == SMLP_FP16 ? launch_mode<GM_DOWN_F16>(gp, args, s) : launch_mode<GM_DOWN_BF16>(gp, args, s);
+    if (p.h_dtype != SMLP_FP16) return launch_mode<GM_DOWN_BF16>(gp, args, s);
+    return p.wd16_bytes ? launch_mode<GM_DOWN_F16W>(gp, args, s) : launch_mode<GM_DOWN_F16>(gp, args, s);
   };
   if (p.dn_split) {
     // Columns [0, dn_split) with the main tile, then the rest with the tail tile: each
@@ -504,7 +513,7 @@ int launch_gemm_down(const Plan& p, const void* w_down, void* out, void* ws, hip
     int rc = one_plane(p.gdn, a);
     if (rc) return rc;
     GArgs t = a;
-    t.b = a.b + (size_t)p.dn_split * p.ldwd;
+    t.b = a.b + (size_t)p.dn_split * a.ldb;
     t.N = (int)(p.H - p.dn_split);
     t.b_rows = t.N;
     t.tiles_m = p.gdn_tail.tiles_m;

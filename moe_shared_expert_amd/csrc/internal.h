@@ -20,6 +20,8 @@ struct SkinnyPlan {
   int kslice;    // K elements per workgroup slice (multiple of 64)
   int blocks;    // total workgroups
   int fpw;       // SKINNY_STREAM16: features (gate_up) or rows (down) per workgroup
+  int ttiles;    // SKINNY_STREAM16 token split: workgroups along M, 16 * mt tokens each
+                 // (0 or 1 = none; blocks counts every workgroup)
 };
 
 enum { SKINNY_DIRECT16 = 2, SKINNY_STREAM16 = 3 };
@@ -43,6 +45,8 @@ struct Plan {
   int h_dtype;              // SMLP_FP32, SMLP_BF16, SMLP_BF16_HILO or SMLP_FP16
   size_t h_offset, h_bytes;
   size_t part_offset, part_bytes;   // split-K partial sums
+  size_t wd16_offset, wd16_bytes;   // fp16 copy of w_down [H, I] (dense) when the down stage
+                                    // multiplies fp16 h by pre-converted weights
   size_t workspace_bytes;
   SkinnyPlan gu, dn;
   GemmPlan ggu, gdn;
@@ -50,6 +54,9 @@ struct Plan {
   // in whole rounds of workgroups and the tail plan the rest (split = 0: no split).
   GemmPlan ggu_tail, gdn_tail;
   int64_t gu_split, dn_split;
+  // Large-M path with the gate_up stage run by the weight-streaming kernel split over
+  // tokens (plan gu) instead of the tiled GEMM (ggu).
+  int gu_tsplit;
   int kernels;
   // Weight views (a rank's slice read in place from full weights): rows between a gate
   // row and its up row in w_gate_up (I for whole weights), and the row stride of w_down
@@ -95,5 +102,8 @@ int launch_fp32_down(const Plan& p, const float* w_down, float* out, void* ws, h
 int launch_slice_rank(const void* wgu, const void* wd, void* wgu_r, void* wd_r, int64_t H,
                       int64_t I, int tp, int rank, int elem_bytes, hipStream_t s);
 int launch_rms_rescale(const float* in, uint16_t* out, int64_t M, int64_t H, hipStream_t s);
+// bf16 -> fp16 copy of a rows x cols weight matrix (source row stride ld_src) into a dense
+// destination (aux.hip).
+int launch_bf16_to_f16(const void* src, int64_t ld_src, int64_t rows, int64_t cols, void* dst, hipStream_t s);
 
 }  // namespace smlp

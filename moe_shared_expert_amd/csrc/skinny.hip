@@ -61,8 +61,12 @@ struct SkArgs {
 // rounding remainder rne(h - hi) in the second.
 __device__ __forceinline__ void store_h(void* base, int M, int N, int m, int n, float h,
                                         int planes) {
-  const uint32_t hi = f2bf(h);
   uint16_t* p = reinterpret_cast<uint16_t*>(base);
+  if (planes == 3) {  // one fp16 plane (the format the tiled down stage reads for bf16 outputs)
+    p[(size_t)m * N + n] = (uint16_t)f2h(h);
+    return;
+  }
+  const uint32_t hi = f2bf(h);
   p[(size_t)m * N + n] = (uint16_t)hi;
   if (planes == 2) p[(size_t)M * N + (size_t)m * N + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
 }
@@ -188,6 +192,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   }
   const int f0 = col * a.fpw;
   const int fend = min(a.N, f0 + a.fpw);
+  // Token split (gridDim.z > 1): workgroup z takes tokens [16 MT z, 16 MT (z + 1)); the
+  // workgroups of one feature range are 8 apart in dispatch order when gridDim.x % 8 == 0,
+  // so they share an XCD and its L2 copy of the weights.
+  const int m0 = blockIdx.z * 16 * MT;
   const uint32_t wbytes = ((uint32_t)(a.w_rows - 1) * (uint32_t)a.ldw + (uint32_t)K) * 2u;
   const uint32_t abytes = (uint32_t)a.M * (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, wbytes);
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int m = mt * 16 + 8 * h + lr;
+        const int m = m0 + mt * 16 + 8 * h + lr;
         ao[q * MT + mt][h] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + ch[h] * 16 : abytes;
       }
 
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int m = mt * 16 + lg * 4 + j;
+        const int m = m0 + mt * 16 + lg * 4 + j;
         const float v = acc[t][mt][j];
         if (GU) {
           const float up = __shfl_xor(v, 8, 64);  // column ln ^ 8 of the same row
@@ -559,7 +567,8 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
 template <int MODE>
 static int launch_stage(const SkinnyPlan& sp, const SkArgs& a, hipStream_t s) {
   constexpr bool GU = MODE == MODE_GATE_UP;
-  dim3 grid(sp.blocks / sp.ksplit, sp.ksplit);
+  const int tt = sp.ttiles > 1 ? sp.ttiles : 1;
+  dim3 grid(sp.blocks / (sp.ksplit * tt), sp.ksplit, tt);
   dim3 block(sp.waves * 64);
 #define SMLP_SK(KERNEL)                                                                  \
   if (sp.mt == MT_ && sp.nb == NB_ && sp.waves == W_ && sp.u == U_) {                    \
@@ -620,7 +629,7 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.ldo = a.N;
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset);
   a.out_f32 = 0;
-  a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : 1;
+  a.h_planes = p.h_dtype == SMLP_BF16_HILO ? 2 : p.h_dtype == SMLP_FP16 ? 3 : 1;
   a.fpw = p.gu.fpw;
   a.w_rows = (int)(p.up_off + p.I);
   a.ldw = (int)p.H;

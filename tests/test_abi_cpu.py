@@ -95,12 +95,24 @@ def test_default_threshold_and_gemm_tuning(L):
     # down: 256 x 256 tiles for the columns of three whole rounds over 256 CUs (768 tiles),
     # the last 1024 columns as one round of 128 x 128 tiles (512), a third launch
     assert p["down_blocks"] == 3 * 256 + (8192 // 128) * ((H - 3 * 256 * 256 // (8192 // 256)) // 128)
-    assert p["down_ksplit"] == 1 and p["kernels"] == 3
+    # four launches: gate_up, the fp16 copy of w_down (fp16 h at this M), two down launches
+    assert p["down_ksplit"] == 1 and p["kernels"] == 4
+    assert p["workspace_bytes"] >= 8192 * I * 2 + H * I * 2
+    # below the conversion threshold the weights are converted in registers instead
+    prev = binding.shared_mlp_tune_weight_convert(1 << 30)
+    try:
+        q = binding.shared_mlp_plan(8192, H, I)
+        assert q["kernels"] == 3 and q["workspace_bytes"] < p["workspace_bytes"]
+        assert binding.shared_mlp_plan(8192, H, I, binding.SMLP_BF16, True)["kernels"] == 3   # bf16 h
+    finally:
+        binding.shared_mlp_tune_weight_convert(prev)
+    with pytest.raises(binding.SmlpError):
+        binding.shared_mlp_tune_weight_convert(0)
     # a pinned down tile is never split
     binding.shared_mlp_tune_gemm(1, bm=256, bn=256, wm=2, wn=4, ns=2)
     try:
         p = binding.shared_mlp_plan(8192, H, I)
-        assert p["down_blocks"] == (8192 // 256) * (H // 256) and p["kernels"] == 2
+        assert p["down_blocks"] == (8192 // 256) * (H // 256) and p["kernels"] == 3
     finally:
         binding.shared_mlp_tune_gemm(1)
     try:

@@ -295,7 +295,8 @@ def test_down_column_split_ragged(partial):
     # rounds' columns keep that tile, the ragged remaining columns run as a second launch.
     M, Hh, Ii = 8100, 4360, 4096
     p = binding.shared_mlp_plan(M, Hh, Ii, binding.SMLP_BF16, partial)
-    assert p["path_name"] == "large_m" and p["kernels"] == 3, p
+    # gate_up, the two down launches, and for a bf16 output (fp16 h) the fp16 copy of w_down
+    assert p["path_name"] == "large_m" and p["kernels"] == (3 if partial else 4), p
     x = synth.activations(M, Hh, config=13)
     wgu, wd = synth.layer_weights(Hh, Ii, config=13)
     out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV), partial=partial)
@@ -309,7 +310,8 @@ def test_gate_up_column_split_ragged():
     # launch that writes its columns of h in place.
     M, Hh, Ii = 2000, 7168, 6104
     p = binding.shared_mlp_plan(M, Hh, Ii)
-    assert p["path_name"] == "large_m" and p["kernels"] == 3, p
+    # two gate_up launches, the fp16 copy of w_down (fp16 h), the down GEMM
+    assert p["path_name"] == "large_m" and p["kernels"] == 4, p
     assert p["gate_up_blocks"] == 8 * 32 + 16 * ((Ii - 32 * 128 + 63) // 64), p
     x = synth.activations(M, Hh, config=14)
     wgu, wd = synth.layer_weights(Hh, Ii, config=14)
@@ -497,6 +499,36 @@ def test_stage_entry_points(M):
     torch.cuda.synchronize()
     whole = run_forward(xd, gd, dd)
     assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,Hh,Ii", [(1100, 2048, 1536), (300, 1032, 392)])
+def test_weight_copy_matches_register_conversion(M, Hh, Ii):
+    # fp16 h: the down stage converts w_down to fp16 once into the workspace (one pass) or
+    # its weight fragments in registers; both convert the same values exactly and multiply
+    # in the same order, so the outputs are bit-identical, and both meet the bar
+    x = synth.activations(M, Hh, config=16, copy=M)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=16)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+    prev_thr = binding.shared_mlp_set_large_m_threshold(1)
+    prev = binding.shared_mlp_tune_weight_convert(1)
+    try:
+        p = binding.shared_mlp_plan(M, Hh, Ii)
+        assert p["h_dtype"] == binding.SMLP_FP16 and p["workspace_bytes"] >= Hh * Ii * 2
+        copied = run_forward(xd, gd, dd)
+        ws = workspace_for(M, Hh, Ii, binding.SMLP_BF16)
+        binding.shared_mlp_gate_up_act(xd, gd, ws)
+        staged = torch.full((M, Hh), float("nan"), dtype=torch.bfloat16, device=DEV)
+        binding.shared_mlp_down(dd, staged, ws)
+        binding.shared_mlp_tune_weight_convert(1 << 30)
+        in_regs = run_forward(xd, gd, dd)
+    finally:
+        binding.shared_mlp_tune_weight_convert(prev)
+        binding.shared_mlp_set_large_m_threshold(prev_thr)
+    torch.cuda.synchronize()
+    assert torch.equal(copied.view(torch.int16), in_regs.view(torch.int16))
+    assert torch.equal(staged.view(torch.int16), copied.view(torch.int16))
+    assert_rms_close(copied, ref, BF16_TOL, f"fp16 weight copy M={M}")
 
 
 def test_slice_rank_fp32_bit_exact():
