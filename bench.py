@@ -570,6 +570,15 @@ def measure_ceilings(dev):
     c, w = cyc.double().mean().item(), tic.double().mean().item()
     res["mfma_clock_ghz"] = round(c / (w / 100e6) / 1e9, 3) if w > 0 else None
     res["mfma_frac_of_spec"] = round(res["mfma_tflops"] / roofline.BF16_MFMA_PEAK_TFLOPS, 4)
+    # LDS-read-only loop: 256 workgroups x 8 waves, 8 KB per wave per round
+    lsink = torch.zeros(256 * 512, dtype=torch.float32, device=dev)
+    lcyc = torch.zeros(256, dtype=torch.int64, device=dev)
+    liters = 4096
+    binding.ceiling_lds(256, liters, lsink, lcyc, stream)
+    torch.cuda.synchronize()
+    per_wg = (8 * 8192 * liters) / lcyc.double()
+    res["lds_read_bytes_per_clk_per_cu"] = round(per_wg.median().item(), 1)
+    res["lds_read_bytes_per_clk_per_cu_max"] = round(per_wg.max().item(), 1)
     res["hbm_frac_of_spec"] = round(res["hbm_read_gbs"] / roofline.HBM_PEAK_GBS, 4)
     torch.cuda.empty_cache()
     return res

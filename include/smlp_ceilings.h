@@ -7,6 +7,7 @@
  *   - the rate of a plain streaming read of distinct buffers (HBM), and of a read that
  *     every workgroup makes of one shared, L2-resident region;
  *   - the bf16 matrix-core rate of an MFMA-only loop, and the shader clock it runs at;
+ *   - the LDS read rate of a compute unit (bytes per shader clock);
  *   - the cost of one grid-wide barrier between two streaming phases of one kernel
  *     (the alternative to a second launch when fusing two dependent stages).
  * Conventions are those of smlp.h: device pointers, work enqueued on `stream`, host
@@ -49,6 +50,17 @@ int shared_mlp_ceiling_read(const void* src, size_t src_bytes, int blocks, size_
  */
 int shared_mlp_ceiling_mfma(int blocks, int iters, float* sink, uint64_t* cycles, uint64_t* ticks,
                             hipStream_t stream);
+
+/*
+ * LDS-read-only loop: `blocks` workgroups of 8 waves and 64 KB of LDS each; every wave
+ * issues `iters` rounds of eight independent 16-byte-per-lane LDS reads (8 KB per wave per
+ * round) at bank-conflict-free addresses.  cycles [blocks]: shader-clock cycles of wave
+ * 0's loop (bytes per clock per compute unit = 8 waves * 8 KB * iters / cycles with one
+ * workgroup per compute unit).  sink [blocks * 512] fp32 is written only where needed to
+ * keep the reads live (its contents carry no meaning).  1 <= blocks <= 65535,
+ * 1 <= iters <= 2^24.
+ */
+int shared_mlp_ceiling_lds(int blocks, int iters, float* sink, uint64_t* cycles, hipStream_t stream);
 
 /*
  * Two streaming phases of bytes_per_block each per workgroup (distinct regions of src,

@@ -85,6 +85,7 @@ CEILING_EXPORTS = {
     "shared_mlp_ceiling_empty": (_int, [_int, _vp]),
     "shared_mlp_ceiling_read": (_int, [_vp, _sz, _int, _sz, _int, _vp, _vp]),
     "shared_mlp_ceiling_mfma": (_int, [_int, _int, _vp, _vp, _vp, _vp]),
+    "shared_mlp_ceiling_lds": (_int, [_int, _int, _vp, _vp, _vp]),
     "shared_mlp_ceiling_two_phase": (_int, [_vp, _sz, _int, _sz, _int, _vp, _vp, _vp]),
 }
 # declared in include/smlp_tuning.h
@@ -460,6 +461,15 @@ def ceiling_mfma(blocks: int, iters: int, sink, cycles, ticks, stream=None):
         raise ValueError("sink, cycles and ticks need one element per block")
     _check(lib().shared_mlp_ceiling_mfma(int(blocks), int(iters), _ptr(sink), _ptr(cycles), _ptr(ticks),
                                          _stream(stream, sink.device)))
+
+
+def ceiling_lds(blocks: int, iters: int, sink, cycles, stream=None):
+    if sink.dtype != torch.float32 or cycles.dtype != torch.int64:
+        raise TypeError("sink is fp32, cycles int64")
+    if sink.numel() < blocks * 512 or cycles.numel() < blocks:
+        raise ValueError("sink needs 512 fp32 and cycles one int64 per block")
+    _check(lib().shared_mlp_ceiling_lds(int(blocks), int(iters), _ptr(sink), _ptr(cycles),
+                                        _stream(stream, sink.device)))
 
 
 def ceiling_two_phase(src, blocks: int, bytes_per_block: int, barrier: bool, bar_state, sink, stream=None):

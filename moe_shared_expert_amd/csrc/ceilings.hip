@@ -1,5 +1,5 @@
 // Measurement kernels (smlp_ceilings.h): launch cost, streaming-read rates, the bf16
-// matrix-core rate and clock, and the cost of a grid-wide barrier.
+// matrix-core rate and clock, the LDS read rate, and the cost of a grid-wide barrier.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -72,6 +72,37 @@ __global__ __launch_bounds__(512) void mfma_kernel(int iters, float* sink, uint6
     cycles[blockIdx.x] = c1 - c0;
     ticks[blockIdx.x] = w1 - w0;
   }
+}
+
+// LDS read loop: each wave reads 8 KB of a 64 KB LDS array per round with eight
+// independent 16-byte-per-lane reads (consecutive lanes, consecutive 16-byte slots: no
+// bank conflicts), the block of each read rotating with the round.
+__global__ __launch_bounds__(512) void lds_kernel(int iters, float* sink, uint64_t* cycles) {
+  __shared__ __attribute__((aligned(1024))) u32x4 lds[4096];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4096; i += 512) {
+    const uint32_t v = (uint32_t)i * 2654435761u;
+    lds[i] = u32x4{v, v ^ 1u, v ^ 2u, v ^ 3u};
+  }
+  __syncthreads();
+  u32x4 x = {0u, 0u, 0u, 0u};
+  const uint64_t c0 = clock64();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = (wave * 8 + j + i) & 63;
+      const u32x4 v = lds[blk * 64 + lane];
+      x[0] ^= v[0];
+      x[1] += v[1];
+      x[2] ^= v[2];
+      x[3] += v[3];
+    }
+  }
+  const uint64_t c1 = clock64();
+  if (threadIdx.x == 0) cycles[blockIdx.x] = c1 - c0;
+  const uint32_t s = x[0] ^ x[1] ^ x[2] ^ x[3];
+  if (s == 0x9e3779b9u) sink[blockIdx.x * 512 + threadIdx.x] = 1.f;  // keeps the reads live
+  else if (threadIdx.x == 0) sink[blockIdx.x * 512] = (float)(s & 1023u);
 }
 
 // Grid barrier over all workgroups: the last arrival resets the count and advances the
@@ -153,6 +184,15 @@ int shared_mlp_ceiling_mfma(int blocks, int iters, float* sink, uint64_t* cycles
   (void)hipGetLastError();
   hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(512), 0, stream, iters, sink, cycles, ticks);
   return status(hipGetLastError(), "mfma launch");
+}
+
+int shared_mlp_ceiling_lds(int blocks, int iters, float* sink, uint64_t* cycles, hipStream_t stream) {
+  if (!sink || !cycles) return smlp::set_error(SMLP_ERR_NULL, "sink and cycles must be non-NULL");
+  if (blocks < 1 || blocks > 65535 || iters < 1 || iters > (1 << 24))
+    return smlp::set_error(SMLP_ERR_ARG, "blocks outside [1, 65535] or iters outside [1, 2^24]");
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(lds_kernel, dim3(blocks), dim3(512), 0, stream, iters, sink, cycles);
+  return status(hipGetLastError(), "lds launch");
 }
 
 int shared_mlp_ceiling_two_phase(const void* src, size_t src_bytes, int blocks, size_t bytes_per_block,
