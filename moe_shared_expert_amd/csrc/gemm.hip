@@ -202,22 +202,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Issue one step's loads into stage `buf` (K elements k0 .. k0+63 of the slice).
-  auto issue = [&](int buf, int k0) {
+  // Issue load l of one step (of the LPS per wave: A plane q block i at l = q*AL + i,
+  // then B block i) into stage `buf` (K elements k0 .. k0+63 of the slice).
+  auto issue_one = [&](int buf, int k0, int l) {
     char* st = lds + buf * STAGE;
     const uint32_t kb = (uint32_t)k0 * 2u;
-#pragma unroll
-    for (int q = 0; q < NA; ++q)
-#pragma unroll
-      for (int i = 0; i < AL; ++i) {
-        const bool ok = aoff[i] != abytes && k0 + achk[i] * 8 < kend;
-        buf_ld_lds(arsc[q], st + q * A_BYTES + (i * W + wave) * 1024, ok ? aoff[i] + kb : abytes);
-      }
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
+    if (l < NA * AL) {
+      const int q = l / AL, i = l % AL;
+      const bool ok = aoff[i] != abytes && k0 + achk[i] * 8 < kend;
+      buf_ld_lds(arsc[q], st + q * A_BYTES + (i * W + wave) * 1024, ok ? aoff[i] + kb : abytes);
+    } else {
+      const int i = l - NA * AL;
       const bool ok = boff[i] != bbytes && k0 + bchk[i] * 8 < kend;
       buf_ld_lds(brsc, st + NA * A_BYTES + (i * W + wave) * 1024, ok ? boff[i] + kb : bbytes);
     }
+  };
+  auto issue = [&](int buf, int k0) {
+#pragma unroll
+    for (int l = 0; l < LPS; ++l) issue_one(buf, k0, l);
   };
 
   // 32x32x16 fragments: lane l reads tile row (base + l%32), K chunk 2*ks + l/32.
@@ -226,43 +228,124 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
   const int fsw = chunk_swz(fr);  // row bases are multiples of 32
   constexpr int NFRAG = NA * TM + TN;
   constexpr int NMFMA = NA * TM * TN;
-  // One K step.  Wave tiles with at least as many MFMAs as fragment reads per sub-step
-  // (the 256-wide tiles and 128 x 128 on 4 waves) pin the order with scheduling
-  // barriers: the fragments of sub-step 0 are read first, then the hook issues the next
-  // stage's global loads; each sub-step's MFMAs are interleaved with the fragment reads
-  // of the next sub-step, two reads ahead of each MFMA, so every read has most of a
-  // sub-step of MFMAs to land before its use (left to the compiler, the reads drifted
-  // next to their MFMAs and each waited out an LDS round trip: prefill gate_up 1219 ->
-  // 1175 us, down 674 -> 657 us).  Thinner wave tiles, with too few MFMAs to hide the
-  // reads behind, keep the compiler's schedule (measured slightly faster there).
+  // Wave tiles with at least as many MFMAs as fragment reads per sub-step (the 256-wide
+  // tiles and 128 x 128 on 4 waves) run the pinned schedule below; thinner wave tiles,
+  // with too few MFMAs to hide the reads behind, keep the compiler's schedule.
   constexpr bool PINNED = NMFMA >= NFRAG;
   auto mma = [](u32x4 a, u32x4 b, f32x16 c) {
     if constexpr (F16 || F16W) return mfma32x32x16_f16(a, b, c);
     else return mfma32x32x16(a, b, c);
   };
-  auto compute = [&](int buf, auto&& hook) {
-    const char* st = lds + buf * STAGE;
-    u32x4 fa[2][NA][TM], fb[2][TN];
-    auto read_frag = [&](int slot, int ks, int t) {
-      const int coff = ((2 * ks + fh) ^ fsw) * 16;
-      if (t < NA * TM) {
-        const int q = t / TM, i = t % TM;
-        fa[slot][q][i] = *reinterpret_cast<const u32x4*>(st + q * A_BYTES + ((wm * TM + i) * 32 + fr) * 128 + coff);
-      } else {
-        const int j = t - NA * TM;
-        fb[slot][j] = *reinterpret_cast<const u32x4*>(st + NA * A_BYTES + ((wn * TN + j) * 32 + fr) * 128 + coff);
-      }
+  u32x4 fa[2][NA][TM], fb[2][TN];
+  // Read fragment t of sub-step ks of stage `stage` into slot `slot`.
+  auto read_frag = [&](int stage, int slot, int ks, int t) __attribute__((always_inline)) {
+    const char* st = lds + stage * STAGE;
+    const int coff = ((2 * ks + fh) ^ fsw) * 16;
+    if (t < NA * TM) {
+      const int q = t / TM, i = t % TM;
+      fa[slot][q][i] = *reinterpret_cast<const u32x4*>(st + q * A_BYTES + ((wm * TM + i) * 32 + fr) * 128 + coff);
+    } else {
+      const int j = t - NA * TM;
+      fb[slot][j] = *reinterpret_cast<const u32x4*>(st + NA * A_BYTES + ((wn * TN + j) * 32 + fr) * 128 + coff);
+    }
+  };
+
+  if constexpr (PINNED) {
+    // Pinned schedule, pipelined across K steps.  Each sub-step's MFMAs (fragment slot
+    // `cur`) are interleaved with the reads of the next sub-step's fragments into the
+    // other slot, two reads ahead of each MFMA, so every read has most of a sub-step of
+    // MFMAs to land (left to the compiler, the reads drifted next to their MFMAs and each
+    // waited out an LDS round trip: prefill gate_up 1219 -> 1175 us, down 674 -> 657 us).
+    // The barrier of step kt sits before its last sub-step, once every wave holds that
+    // sub-step's fragments in registers: the last sub-step's MFMAs then cover the barrier
+    // skew, the reads of step kt + 1's first fragments and the global loads of step
+    // kt + NS into the stage just released.  Those loads are spread one or two per MFMA
+    // over that sub-step and the next step's first one (issued in a burst, the eight
+    // waves' 64 loads per compute unit overflowed the texture address queue and held
+    // up MFMA issue).  Loads stay a full step ahead.  M = 8192: gate_up 1173 -> 1148 us,
+    // down 702 -> 688 us against a barrier at the top of each step with the loads in one
+    // burst; spread over three sub-steps instead of two, the last loads came too close
+    // to the barrier that waits for them (1231 us).
+    constexpr int CONV_AT = (NFRAG - 1) / 2 + 3 < NMFMA ? (NFRAG - 1) / 2 + 3 : NMFMA - 1;
+    // MFMAs of slot cur; reads of sub-step rks of stage rstage into slot cur ^ 1; loads
+    // lo .. hi-1 of the step at lk0 into stage lstage (if ld_on), spread over the MFMAs.
+    auto run = [&](int cur, int rstage, int rks, bool ld_on, int lstage, int lk0, int lo, int hi)
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < NA; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int m = (q * TM + i) * TN + j;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+              if (2 * m + r < NFRAG) read_frag(rstage, cur ^ 1, rks, 2 * m + r);
+            acc[i][j] = mma(fa[cur][q][i], fb[cur][j], acc[i][j]);
+            if constexpr (F16) {
+              // fp16 mode: the weight fragments just read are converted a few MFMAs
+              // after their reads, overlapping the matrix core.
+              if (m == CONV_AT) {
+#pragma unroll
+                for (int jj = 0; jj < TN; ++jj) fb[cur ^ 1][jj] = bf16x8_to_f16x8(fb[cur ^ 1][jj]);
+              }
+            }
+            if (ld_on) {
+#pragma unroll
+              for (int l = 0; l < LPS; ++l)
+                if (l >= lo && l < hi && (l - lo) * NMFMA / (hi - lo) == m) issue_one(lstage, lk0, l);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+      for (int t = 2 * NMFMA; t < NFRAG; ++t) read_frag(rstage, cur ^ 1, rks, t);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    if constexpr (!PINNED) {
+    // Steps 0 .. NS-1 fill the ring; step 0 lands; its first fragments.
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      if (st < nk) issue(st, kbeg + st * BK);
+    wait_steps<LPS, NS - 1>(min(NS - 1, nk - 1));
+    block_barrier();
+#pragma unroll
+    for (int t = 0; t < NFRAG; ++t) read_frag(0, 0, 0, t);
+    if constexpr (F16) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[0][j] = bf16x8_to_f16x8(fb[0][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int HALF = LPS / 2;  // loads issued in the last sub-step; the rest in the next step's first
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt % NS;
+      // The second half of step kt + NS - 1's loads (its first half went out in the last
+      // sub-step of step kt - 1; the prologue issued steps 0 .. NS-1 whole).
+      const bool rest = kt >= 1 && kt + NS - 1 < nk;
+      run(0, st, 1, rest, (kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK, HALF, LPS);
+      run(1, st, 2, false, 0, 0, 0, 1);
+      run(0, st, 3, false, 0, 0, 0, 1);
+      // Every wave holds its last fragments of stage st (lgkmcnt 0) and has step kt + 1
+      // in LDS (vmcnt: steps kt + 2 .. kt + NS - 1 may still be in flight); after the
+      // barrier, stage st takes step kt + NS.  (After the last step the reads fetch
+      // fragments of a stage that are never used, and the barrier is a spare one.)
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      wait_steps<LPS, NS - 2>(min(NS - 2, nk - 2 - kt));
+      block_barrier();
+      run(1, (kt + 1) % NS, 0, kt + NS < nk, st, kbeg + (kt + NS) * BK, 0, HALF);
+    }
+  } else {
+    // One K step: the hook issues the next stage's loads, then the compiler schedules
+    // each sub-step's MFMAs with the next sub-step's reads, one read ahead of a share of
+    // the MFMAs.
+    auto compute = [&](int buf, auto&& hook) {
       hook();
 #pragma unroll
-      for (int t = 0; t < NFRAG; ++t) read_frag(0, 0, t);
+      for (int t = 0; t < NFRAG; ++t) read_frag(buf, 0, 0, t);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int cur = ks & 1;
         if (ks < 3) {
 #pragma unroll
-          for (int t = 0; t < NFRAG; ++t) read_frag(cur ^ 1, ks + 1, t);
+          for (int t = 0; t < NFRAG; ++t) read_frag(buf, cur ^ 1, ks + 1, t);
         }
         if constexpr (F16) {
 #pragma unroll
@@ -283,68 +366,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
           }
         }
       }
-    } else {
+    };
+    // NS-stage ring: step kt lives in stage kt % NS; loads run NS-1 steps ahead.
 #pragma unroll
-      for (int t = 0; t < NFRAG; ++t) read_frag(0, 0, t);
-      __builtin_amdgcn_sched_barrier(0);
-      hook();
-      __builtin_amdgcn_sched_barrier(0);
-      // fp16 mode: the weight fragments of sub-step 0 are converted after the global
-      // loads are issued; those of sub-step ks + 1 inside sub-step ks's MFMA stream, a few
-      // MFMAs after their LDS reads (the weight fragments are read last, two per MFMA), so
-      // the conversion overlaps the matrix core instead of preceding it.
-      constexpr int CONV_AT = (NFRAG - 1) / 2 + 3 < NMFMA ? (NFRAG - 1) / 2 + 3 : NMFMA - 1;
-      if constexpr (F16) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[0][j] = bf16x8_to_f16x8(fb[0][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int cur = ks & 1;
-#pragma unroll
-        for (int q = 0; q < NA; ++q)
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const int m = (q * TM + i) * TN + j;
-              if (ks < 3) {
-#pragma unroll
-                for (int r = 0; r < 2; ++r)
-                  if (2 * m + r < NFRAG) read_frag(cur ^ 1, ks + 1, 2 * m + r);
-              }
-              acc[i][j] = mma(fa[cur][q][i], fb[cur][j], acc[i][j]);
-              if constexpr (F16) {
-                if (ks < 3 && m == CONV_AT) {
-#pragma unroll
-                  for (int jj = 0; jj < TN; ++jj) fb[cur ^ 1][jj] = bf16x8_to_f16x8(fb[cur ^ 1][jj]);
-                }
-              }
-              __builtin_amdgcn_sched_barrier(0);
-            }
-        if (ks < 3) {
-#pragma unroll
-          for (int t = 2 * NMFMA; t < NFRAG; ++t) read_frag(cur ^ 1, ks + 1, t);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nk) issue(st, kbeg + st * BK);
+    for (int kt = 0; kt < nk; ++kt) {
+      // Step kt's loads have landed (this wave: vmcnt, allowing the later steps' loads
+      // to stay in flight; all waves: the barrier), and no wave still reads the stage
+      // that the next loads overwrite (it held step kt-1).
+      wait_steps<LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
+      block_barrier();
+      compute(kt % NS, [&] {
+        if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
+      });
     }
-  };
-
-  // NS-stage ring: step kt lives in stage kt % NS; loads run NS-1 steps ahead.
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(st, kbeg + st * BK);
-  for (int kt = 0; kt < nk; ++kt) {
-    // Step kt's loads have landed (this wave: vmcnt, allowing the later steps' loads
-    // to stay in flight; all waves: the barrier), and no wave still reads the stage
-    // that the next loads overwrite (it held step kt-1).
-    wait_steps<LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
-    block_barrier();
-    compute(kt % NS, [&] {
-      if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
-    });
   }
 
   // Epilogue.  32x32 output: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
