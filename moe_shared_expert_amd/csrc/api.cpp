@@ -348,6 +348,12 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!hilo && tiles_for(256, 256) >= 2 * kCUs && K >= 4096) {
     gp.bm = 256;
     gp.bn = 256;
+  } else if (!hilo && stage == 1 && K >= 4096 && tiles_for(256, 256) * 8 >= 7 * kCUs) {
+    // Long-K down stage whose 256 x 256 tiles fill 7/8 of the chip: one tile per compute
+    // unit without a K split beats 128 x 128 tiles, whose 32 x 64 wave tiles read three
+    // fragments per two MFMAs (M = 2048: 237.7 -> 201.6 us; M = 4096: 418.0 -> 375.2 us).
+    gp.bm = 256;
+    gp.bn = 256;
   } else if (!hilo && stage == 0 && K >= 4096 && full256 && tiles_for(256, 256) >= kCUs &&
              tiles_for(256, 256) * 10 >= 7 * kCUs * ((tiles_for(256, 256) + kCUs - 1) / kCUs)) {
     // gate_up whose 256 x 256 tiles fill the chip once with rounds at least 70% full
@@ -438,8 +444,8 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     if (gp.bm == 256 && gp.bn == 128) {
       ks = stage == 0 ? (3 * kCUs + tiles - 1) / tiles : 2;
       if (ks > 4) ks = 4;
-    } else if (gp.bn == 32) {
-      ks = 1;
+    } else if (gp.bn == 32 || (gp.bm == 256 && gp.bn == 256)) {
+      ks = 1;  // (256 x 256: a down stage from 7/8 of a round takes no K split either)
     } else if (gp.bn == 64 && gp.bm == 128) {
       // Few weight tiles (medium M): split K until about 3 (gate_up) or 1.75 (down)
       // workgroups per compute unit stream weights; fp32 partials cost 2 M / K of the
