@@ -485,6 +485,11 @@ bool split_columns(int stage, int64_t M, int64_t N, int64_t K, smlp::GemmPlan* g
   // 328.9 and 3072: 533.7 -> 488.2 us).
   const int64_t rounds = g->tiles / kCUs, slots = (g->tiles + kCUs - 1) / kCUs * kCUs;
   if (rounds < 1 || g->tiles % kCUs == 0 || (slots - g->tiles) * 8 < slots) return false;
+  // Down: only where the last round is under 9/16 full; from there the tail's 128 x 128
+  // tiles cost more than the idle slots (down at M = 4096 and 6144, last round 75% and
+  // 62.5% full: 388.9 and 559.3 us split against 369.8 and 537.9 unsplit; at 3072, 5120,
+  // 7168 and 8192, 31%, 19%, 6% and 50% full, the split saves 42, 59, 63 and 27 us).
+  if (stage == 1 && (g->tiles % kCUs) * 16 >= 9 * kCUs) return false;
   const int64_t width = stage == 0 ? 128 : 256;  // output columns per 256 x 256 tile
   const int64_t cols = rounds * kCUs / g->tiles_m;  // column tiles in whole rounds
   if (cols < 1 || cols >= (N + width - 1) / width) return false;

@@ -108,6 +108,17 @@ def test_default_threshold_and_gemm_tuning(L):
         binding.shared_mlp_tune_weight_convert(prev)
     with pytest.raises(binding.SmlpError):
         binding.shared_mlp_tune_weight_convert(0)
+    # down from 7/8 of a round of 256 x 256 tiles: that tile, no K split; the columns
+    # are split only while the last round is under 9/16 full
+    p = binding.shared_mlp_plan(2048, H, I)           # 224 tiles, no full round
+    assert p["down_blocks"] == 8 * (H // 256) and p["down_ksplit"] == 1
+    for M in (4096, 6144):                             # last round 75% and 62.5% full
+        p = binding.shared_mlp_plan(M, H, I)
+        assert p["down_blocks"] == (M // 256) * (H // 256) and p["down_ksplit"] == 1, (M, p)
+    p = binding.shared_mlp_plan(3072, H, I)           # 336 tiles, last round 31% full: split
+    assert p["down_blocks"] != 12 * (H // 256) and p["kernels"] == 5, p
+    p = binding.shared_mlp_plan(1536, H, I)           # 168 tiles: 128 x 128 tiles instead
+    assert p["down_blocks"] >= (1536 // 128) * (H // 128), p
     # a pinned down tile is never split
     binding.shared_mlp_tune_gemm(1, bm=256, bn=256, wm=2, wn=4, ns=2)
     try:
