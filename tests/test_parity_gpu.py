@@ -428,6 +428,37 @@ def test_every_compiled_tile(stage, tile, partial, ksplit):
     assert_rms_close(out, ref, BF16_TOL, f"stage {stage} tile {tile} ksplit {ksplit} partial {partial}")
 
 
+# Tiles of the down stage when h is two bf16 planes (hi + lo): the default where I < 256 on
+# the tiled path, and forced by the h-format hook at a longer K.  The 128 x 128 tile on
+# 2 x 2 waves runs the pinned cross-step schedule with two activation planes.
+HILO_TILES = [(128, 128, 2, 2, 3), (128, 64, 4, 1, 2), (128, 64, 4, 1, 4)]
+
+
+@pytest.mark.parametrize("ksplit", [1, 3])
+@pytest.mark.parametrize("tile", HILO_TILES)
+@pytest.mark.parametrize("Ii,forced", [(200, False), (1000, True)])
+def test_every_two_plane_down_tile(tile, ksplit, Ii, forced):
+    M, Hh = 300, 1032
+    x = synth.activations(M, Hh, config=15, copy=Ii)
+    wgu, wd = synth.layer_weights(Hh, Ii, config=15)
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    prev = binding.shared_mlp_set_large_m_threshold(1)
+    if forced:
+        binding.shared_mlp_tune_h_format(2)
+    try:
+        binding.shared_mlp_tune_gemm(1, *tile, ksplit=ksplit)
+        p = binding.shared_mlp_plan(M, Hh, Ii)
+        assert p["path_name"] == "large_m" and p["h_dtype"] == binding.SMLP_BF16_HILO, p
+        # K = 200 holds four 64-element steps: three slices round to two of 128
+        assert p["down_ksplit"] == (ksplit if Ii >= 1000 else min(ksplit, 2)), p
+        out = run_forward(x.to(DEV), wgu.to(DEV), wd.to(DEV))
+    finally:
+        binding.shared_mlp_tune_gemm(1)
+        binding.shared_mlp_tune_h_format(0)
+        binding.shared_mlp_set_large_m_threshold(prev)
+    assert_rms_close(out, ref, BF16_TOL, f"two-plane down tile {tile} ksplit {ksplit} I={Ii}")
+
+
 def test_m_zero_leaves_output_untouched():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
     wgu = torch.zeros(2 * 32, 64, dtype=torch.bfloat16, device=DEV)
