@@ -549,16 +549,28 @@ def measure_ceilings(dev):
     # every workgroup reading one shared 1 MiB region (L2-resident after the first touch)
     tl = median(graph_trials(stream, lambda i, st: binding.ceiling_read(src, blocks, 1 << 20, True, sink, st), 16, 5))
     res["l2_shared_read_gbs_per_cu"] = round((1 << 20) / (tl * 1e-6) / 1e9, 1)
-    # two streaming phases of 64 KiB per workgroup, with and without a grid barrier
-    bar = torch.zeros(4, dtype=torch.int32, device=dev)
+    # two streaming phases of 64 KiB per workgroup in one launch: overlapped (no barrier),
+    # behind a one-counter grid barrier, behind a two-level one; and the same two phases
+    # as two dependent launches
+    bar = torch.zeros(binding.CEILING_BAR_WORDS, dtype=torch.int32, device=dev)
     b = 64 << 10
-    tp0 = median(graph_trials(stream, lambda i, st: binding.ceiling_two_phase(
-        src[(i % 8) * 2 * blocks * b:], blocks, b, False, bar, sink, st), 16, 5))
-    tp1 = median(graph_trials(stream, lambda i, st: binding.ceiling_two_phase(
-        src[(i % 8) * 2 * blocks * b:], blocks, b, True, bar, sink, st), 16, 5))
+    tp = [median(graph_trials(stream, lambda i, st: binding.ceiling_two_phase(
+        src[(i % 8) * 2 * blocks * b:], blocks, b, mode, bar, sink, st), 16, 5)) for mode in (0, 1, 2)]
+
+    def two_launches(i, st):
+        base = (i % 8) * 2 * blocks * b
+        binding.ceiling_read(src[base:base + blocks * b], blocks, b, False, sink, st)
+        binding.ceiling_read(src[base + blocks * b:base + 2 * blocks * b], blocks, b, False, sink, st)
+    t2 = median(graph_trials(stream, two_launches, 16, 5))
     torch.cuda.synchronize()
-    res["grid_barrier_us"] = round(tp1 - tp0, 3)
-    res["grid_barrier_timed_out"] = bool(int(bar[2].item()))
+    res["two_phases_overlapped_us"] = round(tp[0], 3)
+    res["two_phases_flat_barrier_us"] = round(tp[1], 3)
+    res["two_phases_two_level_barrier_us"] = round(tp[2], 3)
+    res["two_phases_two_launches_us"] = round(t2, 3)
+    res["grid_barrier_us"] = round(tp[1] - tp[0], 3)
+    res["grid_barrier_two_level_us"] = round(tp[2] - tp[0], 3)
+    res["launch_boundary_us"] = round(t2 - tp[0], 3)
+    res["grid_barrier_timed_out"] = bool(int(bar[128].item()))
     del src
     # MFMA-only loop: 512 workgroups x 8 waves, 512 rounds of 4 independent 32x32x16 MFMAs
     nb, iters = 512, 512

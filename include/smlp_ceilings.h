@@ -64,14 +64,17 @@ int shared_mlp_ceiling_lds(int blocks, int iters, float* sink, uint64_t* cycles,
 
 /*
  * Two streaming phases of bytes_per_block each per workgroup (distinct regions of src,
- * 2 * blocks * bytes_per_block <= src_bytes), separated by a grid-wide barrier when
- * barrier != 0.  The barrier is a counter and a generation word in bar_state
- * (4 uint32: count, generation, error, unused; zero before the first call, left
- * reusable by every call) updated with device-scope atomics; a workgroup waits a
- * bounded time for the others and then sets bar_state[2] = 1 and goes on, so a launch
- * whose workgroups are not all resident at once ends with that flag set instead of
- * hanging.  blocks <= 256 (one workgroup per compute unit of MI355X).
+ * 2 * blocks * bytes_per_block <= src_bytes), separated by nothing (barrier == 0), by a
+ * grid-wide barrier on one counter (barrier == 1), or by a two-level barrier whose
+ * workgroups arrive on 16 group counters and the groups on one more (barrier == 2).  The
+ * counters, a generation word and an error word live in bar_state (SMLP_CEILING_BAR_WORDS
+ * uint32, 16-byte aligned, zero before the first call and left reusable by every call),
+ * updated with device-scope atomics; a workgroup waits a bounded time for the others and
+ * then sets bar_state[128] = 1 and goes on, so a launch whose workgroups are not all
+ * resident at once ends with that flag set instead of hanging.  blocks <= 256 (one
+ * workgroup per compute unit of MI355X).
  */
+#define SMLP_CEILING_BAR_WORDS 1280
 int shared_mlp_ceiling_two_phase(const void* src, size_t src_bytes, int blocks, size_t bytes_per_block,
                                  int barrier, uint32_t* bar_state, float* sink, hipStream_t stream);
 

@@ -472,11 +472,15 @@ def ceiling_lds(blocks: int, iters: int, sink, cycles, stream=None):
                                         _stream(stream, sink.device)))
 
 
-def ceiling_two_phase(src, blocks: int, bytes_per_block: int, barrier: bool, bar_state, sink, stream=None):
-    if bar_state.dtype != torch.int32 or bar_state.numel() < 4:
-        raise TypeError("bar_state is 4 int32")
+CEILING_BAR_WORDS = 1280  # SMLP_CEILING_BAR_WORDS
+
+
+def ceiling_two_phase(src, blocks: int, bytes_per_block: int, barrier: int, bar_state, sink, stream=None):
+    """barrier: 0 none, 1 one counter, 2 two-level (see include/smlp_ceilings.h)."""
+    if bar_state.dtype != torch.int32 or bar_state.numel() < CEILING_BAR_WORDS:
+        raise TypeError(f"bar_state is {CEILING_BAR_WORDS} int32")
     if sink.dtype != torch.float32 or sink.numel() < blocks:
         raise ValueError("sink needs one fp32 per block")
     _check(lib().shared_mlp_ceiling_two_phase(_ptr(src), src.numel() * src.element_size(), int(blocks),
-                                              int(bytes_per_block), int(bool(barrier)), _ptr(bar_state),
+                                              int(bytes_per_block), int(barrier), _ptr(bar_state),
                                               _ptr(sink), _stream(stream, src.device)))

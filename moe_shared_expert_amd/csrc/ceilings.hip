@@ -105,28 +105,70 @@ __global__ __launch_bounds__(512) void lds_kernel(int iters, float* sink, uint64
   else if (threadIdx.x == 0) sink[blockIdx.x * 512] = (float)(s & 1023u);
 }
 
-// Grid barrier over all workgroups: the last arrival resets the count and advances the
-// generation; the others wait for the generation to change, for at most `limit` polls.
-__device__ void grid_barrier(uint32_t* st, int limit) {
+// Grid barriers over all workgroups, on the words of bar_state (uint32, 64 apart so each
+// counter has its own 256-byte block): [0] flat count, [64] generation, [128] error flag,
+// [192] group count, [256 + 64 g] arrivals of group g.  Every wait is bounded: after
+// `limit` polls a workgroup sets the error flag and goes on.
+constexpr int kGroups = 16;  // hierarchical barrier: workgroup b arrives in group b % kGroups
+
+__device__ bool wait_generation(uint32_t* gen_p, uint32_t gen, int limit) {
+  for (int n = 0; __hip_atomic_load(gen_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen;) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++n >= limit) return false;
+  }
+  return true;
+}
+
+// Flat: every workgroup adds to one counter; the last arrival resets it and advances the
+// generation, the others wait for the generation to change.
+__device__ void grid_barrier_flat(uint32_t* st, int limit) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t gen = __hip_atomic_load(&st[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t gen = __hip_atomic_load(&st[64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     const uint32_t prev = __hip_atomic_fetch_add(&st[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
     if (prev == gridDim.x - 1) {
       __hip_atomic_store(&st[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      __hip_atomic_fetch_add(&st[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&st[64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      int n = 0;
-      while (__hip_atomic_load(&st[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++n >= limit) {
-          __hip_atomic_store(&st[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
+      ok = wait_generation(&st[64], gen, limit);
     }
+    if (!ok) __hip_atomic_store(&st[128], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+}
+
+// Hierarchical: workgroups arrive on kGroups counters in parallel; the last arrival of a
+// group arrives on the group counter, whose last arrival advances the generation.  The
+// atomics on one word are serialised where the memory side performs them, so 16 words
+// of 16 arrivals each take about half the time of one word of 256.
+__device__ void grid_barrier_groups(uint32_t* st, int limit) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int g = blockIdx.x % kGroups;
+    const uint32_t members = gridDim.x / kGroups + (g < (int)(gridDim.x % kGroups) ? 1u : 0u);
+    const uint32_t groups = gridDim.x < (unsigned)kGroups ? gridDim.x : (uint32_t)kGroups;
+    const uint32_t gen = __hip_atomic_load(&st[64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    const uint32_t prev = __hip_atomic_fetch_add(&st[256 + 64 * g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+    if (prev == members - 1) {
+      __hip_atomic_store(&st[256 + 64 * g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      const uint32_t top = __hip_atomic_fetch_add(&st[192], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top == groups - 1) {
+        __hip_atomic_store(&st[192], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __hip_atomic_fetch_add(&st[64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        ok = wait_generation(&st[64], gen, limit);
+      }
+    } else {
+      ok = wait_generation(&st[64], gen, limit);
+    }
+    if (!ok) __hip_atomic_store(&st[128], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
@@ -136,7 +178,8 @@ __global__ __launch_bounds__(kWaves * 64) void two_phase_kernel(const char* src,
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kDepth * 1024 + kPad];
   char* ring = lds + (threadIdx.x >> 6) * kDepth * 1024;
   stream_region(src + (size_t)blockIdx.x * per_block, per_block, ring);
-  if (barrier) grid_barrier(st, 1 << 20);
+  if (barrier == 1) grid_barrier_flat(st, 1 << 20);
+  if (barrier == 2) grid_barrier_groups(st, 1 << 20);
   stream_region(src + ((size_t)gridDim.x + blockIdx.x) * per_block, per_block, ring);
   __syncthreads();
   if (threadIdx.x == 0) sink[blockIdx.x] = (float)(unsigned char)lds[blockIdx.x & 1023];
@@ -199,6 +242,7 @@ int shared_mlp_ceiling_two_phase(const void* src, size_t src_bytes, int blocks, 
                                  int barrier, uint32_t* bar_state, float* sink, hipStream_t stream) {
   if (!src || !sink || (barrier && !bar_state))
     return smlp::set_error(SMLP_ERR_NULL, "src, sink (and bar_state with a barrier) must be non-NULL");
+  if (barrier < 0 || barrier > 2) return smlp::set_error(SMLP_ERR_ARG, "barrier outside {0, 1, 2}");
   if ((uintptr_t)src % 16 || (bar_state && (uintptr_t)bar_state % 16))
     return smlp::set_error(SMLP_ERR_ALIGN, "src and bar_state must be 16-byte aligned");
   if (blocks < 1 || blocks > 256 || bad_region(bytes_per_block))
@@ -207,7 +251,7 @@ int shared_mlp_ceiling_two_phase(const void* src, size_t src_bytes, int blocks, 
     return smlp::set_error(SMLP_ERR_SHAPE, "the two phases run past src_bytes");
   (void)hipGetLastError();
   hipLaunchKernelGGL(two_phase_kernel, dim3(blocks), dim3(kWaves * 64), 0, stream, static_cast<const char*>(src),
-                     (uint32_t)bytes_per_block, barrier ? 1 : 0, bar_state, sink);
+                     (uint32_t)bytes_per_block, barrier, bar_state, sink);
   return status(hipGetLastError(), "two-phase launch");
 }
 

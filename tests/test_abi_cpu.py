@@ -345,3 +345,27 @@ def test_last_error_is_per_thread(L):
         t.join()
     assert seen[0] == {(6, "dtype")}, seen[0]
     assert seen[1] == {(3, "x")}, seen[1]
+
+
+def test_ceiling_kernels_validate_before_launch(L):
+    # every case fails host validation, so no HIP call is made (no GPU here)
+    NULL_, SHAPE, ALIGN, ARG = 1, 2, 3, 8
+    p = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    nul = ctypes.c_void_p(0)
+    s = ctypes.c_void_p(0)
+    assert L.shared_mlp_ceiling_empty(0, s) == ARG
+    assert L.shared_mlp_ceiling_empty(65536, s) == ARG
+    assert L.shared_mlp_ceiling_read(nul, 1 << 20, 1, 1024, 0, p, s) == NULL_
+    assert L.shared_mlp_ceiling_read(odd, 1 << 20, 1, 1024, 0, p, s) == ALIGN
+    assert L.shared_mlp_ceiling_read(p, 1 << 20, 1, 1000, 0, p, s) == ARG
+    assert L.shared_mlp_ceiling_read(p, 1 << 20, 2048, 1024, 0, p, s) == SHAPE
+    assert L.shared_mlp_ceiling_mfma(1, 1, nul, p, p, s) == NULL_
+    assert L.shared_mlp_ceiling_mfma(1, 0, p, p, p, s) == ARG
+    assert L.shared_mlp_ceiling_lds(1, 1, p, nul, s) == NULL_
+    assert L.shared_mlp_ceiling_lds(0, 1, p, p, s) == ARG
+    for barrier in (-1, 3):
+        assert L.shared_mlp_ceiling_two_phase(p, 1 << 30, 256, 1024, barrier, p, p, s) == ARG
+    assert L.shared_mlp_ceiling_two_phase(p, 1 << 30, 256, 1024, 2, nul, p, s) == NULL_
+    assert L.shared_mlp_ceiling_two_phase(p, 1 << 30, 257, 1024, 0, p, p, s) == ARG
+    assert L.shared_mlp_ceiling_two_phase(p, 1 << 20, 256, 4096, 0, p, p, s) == SHAPE
