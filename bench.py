@@ -19,9 +19,12 @@ captured once as a hipGraph and replayed for ``trials`` trials (at least 5, and 
 least 200 timed steps in total), each between two HIP events on the launch stream with
 a device synchronisation on both sides; the reported time is the median trial.
 ``value`` is the achieved algorithmic HBM bandwidth (weights + x + out bytes per layer
-/ time per layer).  ``roofline`` reports the dominant stage (gate_up + SiLU-and-mul),
-timed the same way from a graph of that stage alone.  ``cpu_baseline`` times the fp64
-CPU oracle on a bounded sample of the same workload.
+/ time per layer).  ``roofline`` reports the dominant kernel: where the plan runs the
+whole layer as one launch (decode at M <= 16), that kernel, timed by the layer graph
+itself (the gate_up stage alone, from a graph of that stage, is reported beside it);
+otherwise the dominant stage (gate_up + SiLU-and-mul), timed the same way from a graph
+of that stage alone.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -212,6 +215,8 @@ def run_workload(name, steps, warmup, dev, launch="graph"):
         "gate_up_us": gu_us, "gate_up_alg_bytes": gu_alg, "gate_up_gbs": gu_alg / (gu_us * 1e-6) / 1e9,
         "gate_up_flops": 4 * M * H * I_r, "gate_up_tflops": 4 * M * H * I_r / (gu_us * 1e-6) / 1e12,
         "chain_us_per_layer": chain_us,
+        # one launch per layer (the fused decode layer): the layer graph times that kernel
+        "one_launch": plan["kernels"] == 1,
     }
 
 
@@ -380,7 +385,8 @@ def kernel_source_hash():
 
 
 def profiled_traffic(name):
-    """HBM bytes per launch of the dominant kernel (gate_up, or the latent projection)
+    """HBM bytes per launch of the dominant kernel (the one-launch decode layer, gate_up, or
+    the latent projection)
     from the committed rocprofv3 counter summary of this workload
     (profiles/<workload>.md), or None when that summary was taken on different kernel
     sources than the ones built now."""
@@ -390,7 +396,7 @@ def profiled_traffic(name):
         return None
     text = open(path).read()
     m = re.search(r"kernel source hash[^`]*`([0-9a-f]+)`", text)
-    t = re.search(r"(?:gate_up|projection) traffic bytes per launch: (\d+)", text)
+    t = re.search(r"(?:gate_up|projection|layer) traffic bytes per launch: (\d+)", text)
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return int(t.group(1))
@@ -468,6 +474,19 @@ def roofline_entry(name, r, ceil=None):
              "bytes_per_launch": r["gate_up_alg_bytes"], "traffic": profiled_traffic(name)}
         if ceil and ceil.get("mfma_tflops"):
             e["frac_of_measured_ceiling"] = round(r["gate_up_tflops"] / ceil["mfma_tflops"], 4)
+        return e
+    if r.get("one_launch"):
+        # the whole layer is one kernel: it is the dominant (and only) kernel
+        e = {"bound": "hbm", "kernel": "decode_layer_kernel (gate_up + SiLU-and-mul + down, one launch)",
+             "achieved": round(r["gbs"], 1), "peak": roofline.HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": round(r["gbs"] / roofline.HBM_PEAK_GBS, 4),
+             "kernel_us": round(r["us_per_layer"], 3), "bytes_per_launch": r["alg_bytes"],
+             "traffic": profiled_traffic(name),
+             "gate_up_stage_alone": {"kernel_us": round(r["gate_up_us"], 3),
+                                     "achieved": round(r["gate_up_gbs"], 1),
+                                     "frac": round(r["gate_up_gbs"] / roofline.HBM_PEAK_GBS, 4)}}
+        if ceil and ceil.get("hbm_read_gbs"):
+            e["frac_of_measured_ceiling"] = round(r["gbs"] / ceil["hbm_read_gbs"], 4)
         return e
     e = {"bound": "hbm", "kernel": "gate_up + SiLU-and-mul",
          "achieved": round(r["gate_up_gbs"], 1), "peak": roofline.HBM_PEAK_GBS,

@@ -92,7 +92,8 @@ typedef struct {
   int down_ksplit;        /* K-split factor of the down stage                             */
   int gate_up_blocks;     /* workgroups of the gate_up stage's main kernel                */
   int down_blocks;        /* workgroups of the down stage's main kernel                   */
-  int kernels;            /* kernel launches per forward call                             */
+  int kernels;            /* kernel launches per forward call (1 for the one-launch      */
+                          /* decode layer; 2 there on a stream past the 16th per device)  */
 } smlp_plan;
 
 /* Plan of shared_mlp_forward for these sizes.  Host-only; no HIP call. */
@@ -111,7 +112,14 @@ int shared_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int dtype, size_
  *   partial_fp32 nonzero: write fp32 (a TP rank's partial sum); zero: bf16 output
  *   workspace    device scratch of >= shared_mlp_workspace_bytes(...) bytes, 256-byte
  *                aligned; contents on entry are ignored, on exit unspecified
- * Two or three kernels are enqueued on `stream` (see smlp_plan.kernels).
+ * One to five kernels are enqueued on `stream` (see smlp_plan.kernels).  At M <= 16
+ * with bf16 weights the two stages run as one launch whose down workgroups wait
+ * (bounded) for the gate_up workgroups of the same launch; it keeps a few counters per
+ * stream in a static device array (16 streams per GPU; further streams get the
+ * two-launch form).  Calls on one stream, and on different streams, may run as usual;
+ * two replays of one captured graph must not run at the same time (they share the
+ * capturing stream's counters).  If a down workgroup ever gives up waiting, its output
+ * rows are NaN.
  */
 int shared_mlp_forward(const void* x, const void* w_gate_up, const void* w_down, void* out,
                        int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32,

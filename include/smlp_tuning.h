@@ -62,6 +62,18 @@ int shared_mlp_tune_token_split(int mode);
  * Process-wide, for subsequent plans. */
 int64_t shared_mlp_tune_weight_convert(int64_t min_m);
 
+/* One-launch decode layer: where shared_mlp_forward's plan runs the weight-streaming
+ * stages with one plane of h at M <= 16 (the configurations the fused kernel is built
+ * for), both stages go into one grid: the gate_up workgroups first, then the down
+ * workgroups, which take each compute unit as a gate_up workgroup leaves it, issue
+ * their first weight loads and wait (bounded) for all of h before loading it.  mode:
+ * 0 = automatic, 1 = wherever it applies, 2 = never (two launches).  poll_limit: polls
+ * a down workgroup makes before it gives up, writes NaN and flags the error; 0 = the
+ * default (2^18, a fraction of a second), negative = give up at once (to exercise the
+ * failure path).  Results are identical with and without the fusion.  Process-wide,
+ * for subsequent calls.  Returns SMLP_OK or SMLP_ERR_ARG. */
+int shared_mlp_tune_layer_fusion(int mode, int poll_limit);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,7 @@ TUNING_EXPORTS = {
     "shared_mlp_tune_gemm": (_int, [_int, _int, _int, _int, _int, _int, _int]),
     "shared_mlp_tune_h_planes": (_int, [_int]),
     "shared_mlp_tune_h_format": (_int, [_int]),
+    "shared_mlp_tune_layer_fusion": (_int, [_int, _int]),
     "shared_mlp_tune_weight_convert": (_i64, [_i64]),
     "shared_mlp_tune_token_split": (_int, [_int]),
 }
@@ -297,6 +298,10 @@ def shared_mlp_tune_weight_convert(min_m: int) -> int:
     if prev < 0:
         _check(8)
     return prev
+
+
+def shared_mlp_tune_layer_fusion(mode: int = 0, poll_limit: int = 0):
+    _check(lib().shared_mlp_tune_layer_fusion(mode, poll_limit))
 
 
 def shared_mlp_tune_h_format(fmt: int = 0):

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -84,6 +86,35 @@ std::atomic<int> g_h_format{0};
 // Token-split gate_up on the tiled path (0 = automatic, 1 = always where it applies,
 // 2 = never), see shared_mlp_tune_token_split.
 std::atomic<int> g_tsplit{0};
+
+// One-launch decode layer (0 = automatic, 1 = wherever it applies, 2 = never) and the
+// consumer's poll limit, see shared_mlp_tune_layer_fusion.
+std::atomic<int> g_fuse{0};
+std::atomic<int> g_fuse_limit{1 << 18};
+
+// Counter slot of the one-launch decode layer for (device, stream): launches on one
+// stream run one after another and share a slot; each stream gets its own, up to
+// kLayerSyncSlots per device (-1 beyond that: the layer then runs as two launches).
+int layer_sync_slot(hipStream_t stream) {
+  struct Key {
+    int dev;
+    hipStream_t s;
+  };
+  static std::mutex mu;
+  static std::vector<Key> keys;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  int n = 0;
+  for (const Key& k : keys) {
+    if (k.dev != dev) continue;
+    if (k.s == stream) return n;
+    ++n;
+  }
+  if (n >= smlp::kLayerSyncSlots) return -1;
+  keys.push_back({dev, stream});
+  return n;
+}
 
 // Token count from which a large-M down stage with fp16 h converts w_down to fp16 once
 // (into the workspace) instead of converting its weight fragments in registers, see
@@ -566,6 +597,8 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     }
     p->part_bytes = round_up(part, 256);
     p->kernels = 2 + (p->gu.ksplit > 1) + (p->dn.ksplit > 1);
+    // both stages in one launch (one bf16 plane of h, M <= 16): see shared_mlp_tune_layer_fusion
+    if (g_fuse.load() != 2 && smlp::decode_layer_eligible(*p)) p->kernels = 1;
   } else {
     p->path = SMLP_PATH_LARGE_M;
     // h for a bf16 output: one fp16 plane (the down stage converts its bf16 weight
@@ -754,6 +787,12 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
   }
 
   (void)hipGetLastError();  // clear stale state so a failure below is attributed to us
+  if (stage == kBoth && g_fuse.load() != 2 && smlp::decode_layer_eligible(p)) {
+    const int slot = layer_sync_slot(stream);
+    if (slot >= 0)
+      return hip_status(smlp::launch_decode_layer(p, x, wgu, wd, out, ws, slot, g_fuse_limit.load(), stream),
+                        "decode layer launch");
+  }
   if (stage != kDown) {
     switch (p.path) {
       case SMLP_PATH_FP32:
@@ -1055,6 +1094,13 @@ int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ks
   g_tune[stage].waves = waves;
   g_tune[stage].u = u;
   g_tune[stage].ksplit = ksplit;
+  return ok();
+}
+
+int shared_mlp_tune_layer_fusion(int mode, int poll_limit) {
+  if (mode < 0 || mode > 2) return fail(SMLP_ERR_ARG, "mode = %d outside {0, 1, 2}", mode);
+  g_fuse = mode;
+  g_fuse_limit = poll_limit > 0 ? poll_limit : poll_limit == 0 ? 1 << 18 : 0;
   return ok();
 }
 

@@ -68,6 +68,13 @@ struct Plan {
 int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, void* ws,
                           hipStream_t s);
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s);
+// One-launch decode layer (both stages in one grid; skinny.hip): whether plan p has the
+// stage configurations it is built for, and the launch with counter slot `slot` and a
+// consumer wait of at most `limit` polls.  Returns a hipError_t.
+constexpr int kLayerSyncSlots = 16;
+bool decode_layer_eligible(const Plan& p);
+int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, const void* w_down, void* out,
+                        void* ws, int slot, int limit, hipStream_t s);
 
 // Sum K-split partials [ksplit][M][P*N] in slice order and apply the stage epilogue
 // (gate_up: SiLU-and-mul into h, h_fmt 1 = one bf16 plane, 2 = bf16 hi + lo, 3 = fp16;

@@ -29,6 +29,8 @@
 // two planes the down kernel multiplies both (two MFMAs per fragment), so h is
 // effectively not rounded.  The planner picks one plane unless the down contraction
 // is short.
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 #include "smlp.h"
@@ -69,6 +71,20 @@ __device__ __forceinline__ void store_h(void* base, int M, int N, int m, int n, 
   const uint32_t hi = f2bf(h);
   p[(size_t)m * N + n] = (uint16_t)hi;
   if (planes == 2) p[(size_t)M * N + (size_t)m * N + n] = (uint16_t)f2bf(h - __uint_as_float(hi << 16));
+}
+
+// One bf16 plane of h stored agent-coherent (write-through past this XCD's L2), for a
+// consumer on another XCD in the same launch.
+__device__ __forceinline__ void store_h_coherent(void* base, int M, int N, int m, int n, float h) {
+  (void)M;
+  __hip_atomic_store(reinterpret_cast<uint16_t*>(base) + (size_t)m * N + n, (uint16_t)f2bf(h), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Direct buffer-to-LDS load that misses in this XCD's L2 when the line may be stale
+// (agent-coherent), to read data another XCD wrote in the same launch.
+__device__ __forceinline__ void buf_ld_lds_coherent(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 16);
 }
 
 // LDS bytes the cross-wave reduction needs.
@@ -144,7 +160,7 @@ __device__ __forceinline__ void finish_workgroup(const SkArgs& a,
 }
 
 // Streaming kernel (M <= 32).  A workgroup owns the contiguous feature range
-// [blockIdx.x * fpw, +fpw) and a K slice; the range is cut into NT 16-row MFMA tiles.
+// [col * fpw, +fpw) and a K slice; the range is cut into NT 16-row MFMA tiles.
 // gate_up tiles pack 8 features: rows 0-7 are their gate rows and rows 8-15 their up
 // rows; down tiles are 16 consecutive rows.  The K slice is interleaved over the waves
 // in 64-element steps.  Each operand block reaches a wave-private LDS ring by direct
@@ -157,19 +173,70 @@ __device__ __forceinline__ void finish_workgroup(const SkArgs& a,
 // to the wave, so the loop needs no barrier.  Steps past the slice load zeros (no
 // memory traffic), so the loop issues ahead without branches.
 template <int MT, int NT, int WAVES, int STAGES, int MODE>
-__global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
+constexpr int stream_lds_bytes() {
+  constexpr int NA = MODE == MODE_DOWN_HILO ? 2 : 1;
+  constexpr int WAVE_LDS = STAGES * (NT + NA * MT) * 2048;
+  constexpr int RED_LDS = lds_red_bytes<MT, NT, WAVES, false>();
+  return WAVES * WAVE_LDS > RED_LDS ? WAVES * WAVE_LDS : RED_LDS;
+}
+
+// s_waitcnt vmcnt(n) for an n known only after unrolling (0 <= n <= MAX).
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (MAX == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAX) wait_vmcnt<MAX>();
+    else wait_vmcnt_le<MAX - 1>(n);
+  }
+}
+
+// Role of a streaming stage inside the one-launch decode layer (decode_layer_kernel):
+// none (a stage of its own), the gate_up producer (h stored agent-coherent), or the
+// down consumer (weight loads issued before h is ready; h loaded agent-coherent).
+enum { FUSE_NONE = 0, FUSE_PRODUCER = 1, FUSE_CONSUMER = 2 };
+
+struct StreamSync {
+  const uint32_t* ready;  // consumer: its ready flag
+  uint32_t target;        // consumer: the flag value that means h is complete
+  int limit;              // consumer: polls before giving up
+  int* flag;              // consumer: an LDS word outside the ring
+};
+
+// Wait (thread 0 polling, the workgroup behind a barrier) until *sy.ready holds
+// sy.target, for at most sy.limit polls; returns false if it gave up.
+__device__ __forceinline__ bool wait_ready(const StreamSync& sy) {
+  if (threadIdx.x == 0) {
+    bool ok = false;
+    for (int n = 0; n < sy.limit; ++n) {
+      if (__hip_atomic_load(sy.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sy.target) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+    *reinterpret_cast<volatile int*>(sy.flag) = ok;
+  }
+  __syncthreads();
+  return *reinterpret_cast<volatile int*>(sy.flag) != 0;
+}
+
+template <int MT, int NT, int WAVES, int STAGES, int MODE, int FUSE>
+__device__ __forceinline__ void stream_body(const SkArgs& a, char* lds, int col, int slice, int ksplit,
+                                            int m0, const StreamSync& sy) {
   constexpr bool GU = MODE == MODE_GATE_UP;
   constexpr int NA = MODE == MODE_DOWN_HILO ? 2 : 1;  // activation planes: x, or h hi + lo
   constexpr int TA = NA * MT;           // activation tiles per K step
   constexpr int TT = NT + TA;           // 2 KB tiles per K step
   constexpr int SLOT = TT * 2048;       // one ring slot: one K step of this wave
   constexpr int WAVE_LDS = STAGES * SLOT;
-  constexpr int LPS = 2 * TT;           // 1 KB loads per K step
-  constexpr int RED_LDS = lds_red_bytes<MT, NT, WAVES, false>();
-  constexpr int LDS_BYTES = WAVES * WAVE_LDS > RED_LDS ? WAVES * WAVE_LDS : RED_LDS;
+  constexpr int LW = 2 * NT, LA = 2 * TA;  // 1 KB weight / activation loads per K step
+  constexpr int LPS = LW + LA;             // 1 KB loads per K step
+  constexpr int LDS_BYTES = stream_lds_bytes<MT, NT, WAVES, STAGES, MODE>();
   static_assert(STAGES >= 2 && LPS * (STAGES - 1) < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  static_assert(FUSE != FUSE_CONSUMER || (LPS * STAGES < 64 && MODE != MODE_GATE_UP), "consumer ring");
+  static_assert(FUSE != FUSE_PRODUCER || MODE == MODE_GATE_UP, "producer stage");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -178,24 +245,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   const int K = a.K;
   char* my = lds + wave * WAVE_LDS;
 
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  With
-  // a K split, the (slice, column) order is cut into one contiguous run per XCD, so an
-  // XCD holds whole K slices and fetches only its slices of the activations.
-  int col = blockIdx.x, slice = blockIdx.y;
-  if (gridDim.y > 1) {
-    const int total = gridDim.x * gridDim.y;
-    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
-    const int xcd = lin % 8, per = total / 8, rem = total % 8;
-    const int t = xcd * per + min(xcd, rem) + lin / 8;
-    slice = t / gridDim.x;
-    col = t % gridDim.x;
-  }
   const int f0 = col * a.fpw;
   const int fend = min(a.N, f0 + a.fpw);
-  // Token split (gridDim.z > 1): workgroup z takes tokens [16 MT z, 16 MT (z + 1)); the
-  // workgroups of one feature range are 8 apart in dispatch order when gridDim.x % 8 == 0,
-  // so they share an XCD and its L2 copy of the weights.
-  const int m0 = blockIdx.z * 16 * MT;
   const uint32_t wbytes = ((uint32_t)(a.w_rows - 1) * (uint32_t)a.ldw + (uint32_t)K) * 2u;
   const uint32_t abytes = (uint32_t)a.M * (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, wbytes);
@@ -244,25 +295,34 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   constexpr int STEP = 64 * WAVES;
   const int nst = (kend - kbeg + STEP - 1) / STEP;
 
-  // Issue K step i of this wave into ring slot `slot`.
-  auto issue = [&](int slot, int i) {
+  // Issue the weight or activation loads of K step i of this wave into ring slot `slot`.
+  auto issue_w = [&](int slot, int i) {
     const int k = kbeg + (i * WAVES + wave) * 64;
     const uint32_t kb = (uint32_t)k * 2u;
     char* sl = my + slot * SLOT;
-    bool kok[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) kok[h] = k + ch[h] * 8 < kend;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        buf_ld_lds_nt(wr, sl + t * 2048 + h * 1024, (kok[h] && wo[t][h] != wbytes) ? wo[t][h] + kb : wbytes);
+        buf_ld_lds_nt(wr, sl + t * 2048 + h * 1024,
+                      (k + ch[h] * 8 < kend && wo[t][h] != wbytes) ? wo[t][h] + kb : wbytes);
+  };
+  auto issue_a = [&](int slot, int i) {
+    const int k = kbeg + (i * WAVES + wave) * 64;
+    const uint32_t kb = (uint32_t)k * 2u;
+    char* sl = my + slot * SLOT;
 #pragma unroll
     for (int t = 0; t < TA; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        buf_ld_lds(ar[t / MT], sl + (NT + t) * 2048 + h * 1024,
-                   (kok[h] && ao[t][h] != abytes) ? ao[t][h] + kb : abytes);
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = (k + ch[h] * 8 < kend && ao[t][h] != abytes) ? ao[t][h] + kb : abytes;
+        if constexpr (FUSE == FUSE_CONSUMER) buf_ld_lds_coherent(ar[t / MT], sl + (NT + t) * 2048 + h * 1024, off);
+        else buf_ld_lds(ar[t / MT], sl + (NT + t) * 2048 + h * 1024, off);
+      }
+  };
+  auto issue = [&](int slot, int i) {
+    issue_w(slot, i);
+    issue_a(slot, i);
   };
   // Multiply the K step in ring slot `slot`: 16x16x32 fragments, lane (ln, lg) reads
   // tile row ln, chunk 4j + lg.
@@ -286,10 +346,33 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
     }
   };
 
-#pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p) issue(p, p);
   int slot = 0;  // ring slot of step i
-  for (int i = 0; i < nst; ++i) {
+  int i0 = 0;
+  bool ready = true;
+  if constexpr (FUSE == FUSE_CONSUMER) {
+    // The weights do not depend on h: the weight blocks of the first STAGES steps (the
+    // whole ring) go out before the wait, then the matching h blocks.  Loads complete in
+    // issue order, so step i < STAGES - 1 waits with the h blocks of steps i + 1 ..
+    // STAGES - 1 and the i steps issued since still in flight; from step STAGES - 1 on,
+    // the loop below runs as usual.
+#pragma unroll
+    for (int p = 0; p < STAGES; ++p) issue_w(p, p);
+    ready = wait_ready(sy);
+#pragma unroll
+    for (int p = 0; p < STAGES; ++p) issue_a(p, p);
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i) {
+      if (i >= 1) issue(i - 1, i + STAGES - 1);
+      wait_vmcnt_le<LPS * (STAGES - 1)>((STAGES - 1 - i) * LA + i * LPS);
+      if (i < nst) compute(i);
+    }
+    slot = STAGES - 1;
+    i0 = STAGES - 1;
+  } else {
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p) issue(p, p);
+  }
+  for (int i = i0; i < nst; ++i) {
     // The slot of step i - 1 (multiplied in the previous iteration) takes step
     // i + STAGES - 1; then wait until step i has landed, STAGES - 1 later steps may
     // stay in flight.
@@ -326,7 +409,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
   if (wave != 0) return;
 
   // Epilogue.  MFMA output: lane (ln, lg), element j = (token mt*16 + 4*lg + j, column ln).
-  const int ksplit = gridDim.y;
+  // A consumer whose wait gave up writes NaN.
+  const float poison = ready ? 0.f : __builtin_nanf("");
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -343,20 +427,124 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
             // lanes 0-7 hold gate columns, lanes 8-15 the matching up columns
             a.part[((size_t)slice * a.M + m) * (size_t)(2 * a.N) + (ln < 8 ? f : a.N + f)] = v;
           } else if (ln < 8) {
-            store_h(a.out, a.M, a.N, m, f, silu_mul(v, up), a.h_planes);
+            if constexpr (FUSE == FUSE_PRODUCER) store_h_coherent(a.out, a.M, a.N, m, f, silu_mul(v, up));
+            else store_h(a.out, a.M, a.N, m, f, silu_mul(v, up), a.h_planes);
           }
         } else {
           const int n = f0 + 16 * t + ln;
           if (m >= a.M || n >= fend) continue;
           if (ksplit > 1)
-            a.part[((size_t)slice * a.M + m) * (size_t)a.N + n] = v;
+            a.part[((size_t)slice * a.M + m) * (size_t)a.N + n] = v + poison;
           else if (a.out_f32)
-            reinterpret_cast<float*>(a.out)[(size_t)m * a.ldo + n] = v;
+            reinterpret_cast<float*>(a.out)[(size_t)m * a.ldo + n] = v + poison;
           else
-            reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] = (uint16_t)f2bf(v);
+            reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] = (uint16_t)f2bf(v + poison);
         }
       }
 }
+
+template <int MT, int NT, int WAVES, int STAGES, int MODE>
+__global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[stream_lds_bytes<MT, NT, WAVES, STAGES, MODE>()];
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  With
+  // a K split, the (slice, column) order is cut into one contiguous run per XCD, so an
+  // XCD holds whole K slices and fetches only its slices of the activations.
+  int col = blockIdx.x, slice = blockIdx.y;
+  if (gridDim.y > 1) {
+    const int total = gridDim.x * gridDim.y;
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = lin % 8, per = total / 8, rem = total % 8;
+    const int t = xcd * per + min(xcd, rem) + lin / 8;
+    slice = t / gridDim.x;
+    col = t % gridDim.x;
+  }
+  // Token split (gridDim.z > 1): workgroup z takes tokens [16 MT z, 16 MT (z + 1)); the
+  // workgroups of one feature range are 8 apart in dispatch order when gridDim.x % 8 == 0,
+  // so they share an XCD and its L2 copy of the weights.
+  stream_body<MT, NT, WAVES, STAGES, MODE, FUSE_NONE>(a, lds, col, slice, gridDim.y, blockIdx.z * 16 * MT,
+                                                     StreamSync{});
+}
+
+// One-launch decode layer: the gate_up stage (producers, blockIdx.x < producers, 4
+// waves) and the down projection over one bf16 plane of h (consumers, 8 waves) in one
+// grid.  Workgroups are dispatched in index order, so every producer has been placed
+// on a compute unit before any consumer, and a consumer only waits for producers,
+// which wait for nothing: the launch cannot deadlock, whatever else shares the GPU.
+// A consumer starts on a compute unit as soon as a producer leaves it, issues its
+// first weight loads, and waits until h is complete before it loads h.  Producers
+// store h agent-coherent and count themselves once their stores are complete;
+// consumers load h agent-coherent.
+//
+// Counters (one slot per stream, words 256 bytes apart so that no memory channel takes
+// all the traffic): [64 g] producers of group g done (g < 16, producer b in group
+// b % 16), [64 * 16] groups done, [64 * (17 + f)] ready flag f (f < 16, consumer c polls
+// flag c % 16), [64 * 33] consumers done, [64 * 34] the slot's generation G.  Every
+// workgroup reads G when it starts; G only changes when the last consumer ends, after
+// every workgroup has read it.  The last producer of a group clears the group's count,
+// the last group clears the groups' count and stores G + 1 in every ready flag, and the
+// last consumer clears the consumers' count and stores G + 1 in the generation, so the
+// slot is ready for the next launch on the same stream without being cleared from the
+// host.  A consumer that gives up waiting (limit polls) writes NaN.
+constexpr int kSyncGroups = 16;
+constexpr int kSyncWords = 64 * 35;
+
+template <int MT, int NTG, int SG, int NTD, int SD>
+__global__ __launch_bounds__(512) void decode_layer_kernel(SkArgs gu, SkArgs dn, uint32_t* sync, int producers,
+                                                           int limit) {
+  constexpr int LG = stream_lds_bytes<MT, NTG, 4, SG, MODE_GATE_UP>();
+  constexpr int LD = stream_lds_bytes<MT, NTD, 8, SD, MODE_LINEAR>();
+  // The consumer's ready flag sits in a 1 KB pad after the rings: a workgroup LDS size
+  // that is not a whole number of KB (a separate 4-byte variable) slowed the streaming
+  // loops by ~10% on MI355X (gate_up phase 26.6 -> 29.8 us at M = 16).
+  constexpr int RING = LG > LD ? LG : LD;
+  __shared__ __attribute__((aligned(1024))) char lds[RING + 1024];
+  int& flag = *reinterpret_cast<int*>(lds + RING);
+  uint32_t* const gen_word = sync + 64 * 34;
+  if ((int)blockIdx.x < producers) {
+    if (threadIdx.x >= 256) return;
+    uint32_t gen = 0;
+    if (threadIdx.x == 0) gen = __hip_atomic_load(gen_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stream_body<MT, NTG, 4, SG, MODE_GATE_UP, FUSE_PRODUCER>(gu, lds, blockIdx.x, 0, 1, 0, StreamSync{});
+    if (threadIdx.x < 64) {  // wave 0 wrote h
+      wait_vmcnt<0>();
+      if (threadIdx.x == 0) {
+        const int g = blockIdx.x % kSyncGroups;
+        const uint32_t members = producers / kSyncGroups + (g < producers % kSyncGroups ? 1u : 0u);
+        const uint32_t groups = producers < kSyncGroups ? producers : kSyncGroups;
+        const uint32_t prev = __hip_atomic_fetch_add(sync + 64 * g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == members - 1) {
+          __hip_atomic_store(sync + 64 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t top =
+              __hip_atomic_fetch_add(sync + 64 * kSyncGroups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (top == groups - 1) {
+            __hip_atomic_store(sync + 64 * kSyncGroups, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int f = 0; f < kSyncGroups; ++f)
+              __hip_atomic_store(sync + 64 * (17 + f), gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+    return;
+  }
+  const int c = blockIdx.x - producers;
+  const uint32_t consumers = gridDim.x - (uint32_t)producers;
+  // Thread 0 polls and ends the workgroup's part, so only it reads the generation.
+  uint32_t gen = 0;
+  if (threadIdx.x == 0) gen = __hip_atomic_load(gen_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const StreamSync sy{sync + 64 * (17 + c % kSyncGroups), gen + 1u, limit, &flag};
+  stream_body<MT, NTD, 8, SD, MODE_LINEAR, FUSE_CONSUMER>(dn, lds, c, 0, 1, 0, sy);
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(sync + 64 * 33, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == consumers - 1) {
+      __hip_atomic_store(sync + 64 * 33, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gen_word, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Counter slots of the one-launch decode layer (one per stream that uses it, per device).
+__device__ uint32_t g_layer_sync[kLayerSyncSlots * kSyncWords];
 
 // Direct-load variant for larger token tiles (MT >= 4), where staging every
 // activation tile through LDS per wave would not fit: operands are loaded straight
@@ -636,6 +824,79 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
   if (rc || p.gu.ksplit == 1) return rc;
   return launch_finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);
+}
+
+// Device address of this device's counter slots, looked up once per device.
+static int layer_sync_base(uint32_t** out) {
+  static std::mutex mu;
+  static uint32_t* base[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    e = hipGetSymbolAddress((void**)&base[dev], HIP_SYMBOL(g_layer_sync));
+    if (e != hipSuccess) {
+      base[dev] = nullptr;
+      return (int)e;
+    }
+  }
+  *out = base[dev];
+  return (int)hipSuccess;
+}
+
+bool decode_layer_eligible(const Plan& p) {
+  const SkinnyPlan& g = p.gu;
+  const SkinnyPlan& d = p.dn;
+  return p.path == SMLP_PATH_SMALL_M && p.h_dtype == SMLP_BF16 && g.kind == SKINNY_STREAM16 && g.mt == 1 &&
+         g.nb == 3 && g.waves == 4 && g.u == 3 && g.ksplit == 1 && g.ttiles <= 1 && d.kind == SKINNY_STREAM16 &&
+         d.mt == 1 && d.nb == 2 && d.waves == 8 && d.u == 3 && d.ksplit == 1 && g.blocks + d.blocks <= 65535;
+}
+
+int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, const void* w_down, void* out,
+                        void* ws, int slot, int limit, hipStream_t s) {
+  if (!decode_layer_eligible(p) || slot < 0 || slot >= kLayerSyncSlots) return (int)hipErrorInvalidConfiguration;
+  SkArgs g;
+  g.a_hi = reinterpret_cast<const uint16_t*>(x);
+  g.a_lo = nullptr;
+  g.w = reinterpret_cast<const uint16_t*>(w_gate_up);
+  g.M = (int)p.M;
+  g.K = (int)p.H;
+  g.N = (int)p.I;
+  g.up_off = (int)p.up_off;
+  g.kslice = p.gu.kslice;
+  g.out = static_cast<char*>(ws) + p.h_offset;
+  g.ldo = g.N;
+  g.part = nullptr;
+  g.out_f32 = 0;
+  g.h_planes = 1;
+  g.fpw = p.gu.fpw;
+  g.w_rows = (int)(p.up_off + p.I);
+  g.ldw = (int)p.H;
+  SkArgs d;
+  d.a_hi = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.h_offset);
+  d.a_lo = nullptr;
+  d.w = reinterpret_cast<const uint16_t*>(w_down);
+  d.M = (int)p.M;
+  d.K = (int)p.I;
+  d.N = (int)p.H;
+  d.up_off = 0;
+  d.kslice = p.dn.kslice;
+  d.out = out;
+  d.ldo = (int)p.H;
+  d.part = nullptr;
+  d.out_f32 = p.partial_fp32 ? 1 : 0;
+  d.h_planes = 1;
+  d.fpw = p.dn.fpw;
+  d.w_rows = (int)p.H;
+  d.ldw = (int)p.ldwd;
+  uint32_t* sync = nullptr;
+  const int rc = layer_sync_base(&sync);
+  if (rc != (int)hipSuccess) return rc;
+  hipLaunchKernelGGL((decode_layer_kernel<1, 3, 3, 2, 3>), dim3(p.gu.blocks + p.dn.blocks), dim3(512), 0, s, g, d,
+                     sync + (size_t)slot * kSyncWords, p.gu.blocks, limit);
+  return (int)hipGetLastError();
 }
 
 int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, hipStream_t s) {

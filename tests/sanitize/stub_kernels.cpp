@@ -9,6 +9,10 @@ namespace smlp {
 
 int launch_skinny_gate_up(const Plan&, const void*, const void*, void*, hipStream_t) { return (int)hipErrorNotReady; }
 int launch_skinny_down(const Plan&, const void*, void*, void*, hipStream_t) { return (int)hipErrorNotReady; }
+bool decode_layer_eligible(const Plan&) { return false; }
+int launch_decode_layer(const Plan&, const void*, const void*, const void*, void*, void*, int, int, hipStream_t) {
+  return (int)hipErrorNotReady;
+}
 int launch_finalize(bool, const float*, int, int, int, void*, int, int, int, hipStream_t) { return (int)hipErrorNotReady; }
 int launch_skinny_linear(const SkinnyPlan&, const void*, const void*, void*, int, int, int, int, int, float*,
                          hipStream_t, int) {

@@ -369,3 +369,28 @@ def test_ceiling_kernels_validate_before_launch(L):
     assert L.shared_mlp_ceiling_two_phase(p, 1 << 30, 256, 1024, 2, nul, p, s) == NULL_
     assert L.shared_mlp_ceiling_two_phase(p, 1 << 30, 257, 1024, 0, p, p, s) == ARG
     assert L.shared_mlp_ceiling_two_phase(p, 1 << 20, 256, 4096, 0, p, p, s) == SHAPE
+
+
+def test_layer_fusion_plan_and_hook(L):
+    """The one-launch decode layer: one kernel for the fused configuration (M <= 16, one
+    plane of h, the Kimi-K3 stage tiles), two when it is switched off or does not apply;
+    the hook validates its mode before any state changes."""
+    try:
+        for M in (1, 8, 16):
+            assert binding.shared_mlp_plan(M, H, I)["kernels"] == 1
+            assert binding.shared_mlp_plan(M, H, I, BF16, True)["kernels"] == 1
+        assert binding.shared_mlp_plan(32, H, I)["kernels"] == 2      # two token tiles
+        assert binding.shared_mlp_plan(16, H, 128)["kernels"] >= 2     # two planes of h
+        binding.shared_mlp_tune_h_planes(2)
+        assert binding.shared_mlp_plan(16, H, I)["kernels"] == 2
+        binding.shared_mlp_tune_h_planes(0)
+        binding.shared_mlp_tune_layer_fusion(2, 0)
+        assert binding.shared_mlp_plan(16, H, I)["kernels"] == 2
+        binding.shared_mlp_tune_layer_fusion(1, 1000)
+        assert binding.shared_mlp_plan(16, H, I)["kernels"] == 1
+        for bad in (-1, 3):
+            with pytest.raises(binding.SmlpError):
+                binding.shared_mlp_tune_layer_fusion(bad, 0)
+    finally:
+        binding.shared_mlp_tune_h_planes(0)
+        binding.shared_mlp_tune_layer_fusion(0, 0)

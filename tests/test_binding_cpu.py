@@ -137,7 +137,7 @@ def test_every_unpinned_plan_succeeds(L, threshold):
                 continue
             try:
                 p = binding.shared_mlp_plan(M, H, I, binding.SMLP_BF16, partial)
-                assert p["workspace_bytes"] >= 0 and p["kernels"] >= 2
+                assert p["workspace_bytes"] >= 0 and p["kernels"] >= 1
             except binding.SmlpError as e:
                 failed.append((M, H, I, partial, str(e)))
     finally:
