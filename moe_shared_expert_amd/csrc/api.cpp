@@ -92,29 +92,7 @@ std::atomic<int> g_tsplit{0};
 std::atomic<int> g_fuse{0};
 std::atomic<int> g_fuse_limit{1 << 18};
 
-// Counter slot of the one-launch decode layer for (device, stream): launches on one
-// stream run one after another and share a slot; each stream gets its own, up to
-// kLayerSyncSlots per device (-1 beyond that: the layer then runs as two launches).
-int layer_sync_slot(hipStream_t stream) {
-  struct Key {
-    int dev;
-    hipStream_t s;
-  };
-  static std::mutex mu;
-  static std::vector<Key> keys;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  std::lock_guard<std::mutex> lock(mu);
-  int n = 0;
-  for (const Key& k : keys) {
-    if (k.dev != dev) continue;
-    if (k.s == stream) return n;
-    ++n;
-  }
-  if (n >= smlp::kLayerSyncSlots) return -1;
-  keys.push_back({dev, stream});
-  return n;
-}
+int layer_sync_slot(hipStream_t stream) { return smlp::stream_slot(stream); }
 
 // Token count from which a large-M down stage with fp16 h converts w_down to fp16 once
 // (into the workspace) instead of converting its weight fragments in registers, see
@@ -596,7 +574,13 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
       if (d > part) part = d;
     }
     p->part_bytes = round_up(part, 256);
-    p->kernels = 2 + (p->gu.ksplit > 1) + (p->dn.ksplit > 1);
+    // a K-split streaming stage reduces in its own launch (the last-arriving slice of a
+    // column applies the epilogue) when there are at most 256 columns; else a finalize launch
+    auto finalize_launch = [](const smlp::SkinnyPlan& sp) {
+      const int cols = sp.blocks / (sp.ksplit * (sp.ttiles > 1 ? sp.ttiles : 1));
+      return sp.ksplit > 1 && !(g_fuse.load() != 2 && sp.kind == smlp::SKINNY_STREAM16 && cols <= 256);
+    };
+    p->kernels = 2 + finalize_launch(p->gu) + finalize_launch(p->dn);
     // both stages in one launch (one bf16 plane of h, M <= 16): see shared_mlp_tune_layer_fusion
     if (g_fuse.load() != 2 && smlp::decode_layer_eligible(*p)) p->kernels = 1;
   } else {
@@ -822,6 +806,33 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
 }  // namespace
 
 namespace smlp {
+// Counter slot of a stream (one-launch decode layer, in-launch K-split reductions):
+// launches on one stream run one after another and share a slot; each stream gets its
+// own, up to kLayerSyncSlots per device (-1 beyond that: those stages then run as
+// separate launches).
+int stream_slot(hipStream_t stream) {
+  struct Key {
+    int dev;
+    hipStream_t s;
+  };
+  static std::mutex mu;
+  static std::vector<Key> keys;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  int n = 0;
+  for (const Key& k : keys) {
+    if (k.dev != dev) continue;
+    if (k.s == stream) return n;
+    ++n;
+  }
+  if (n >= smlp::kLayerSyncSlots) return -1;
+  keys.push_back({dev, stream});
+  return n;
+}
+
+bool fusion_enabled() { return g_fuse.load() != 2; }
+
 // Status setter shared with the other host-only translation units (layout.cpp).
 int set_error(int status, const char* msg) {
   if (status == SMLP_OK) return ok();
@@ -945,7 +956,8 @@ int shared_mlp_linear_plan(int64_t M, int64_t K, int64_t N, smlp_plan* plan) {
   plan->workspace_bytes = lp.part_bytes;
   plan->down_ksplit = lp.path == SMLP_PATH_NONE ? 1 : lp.ksplit;
   plan->down_blocks = lp.blocks;
-  plan->kernels = lp.path == SMLP_PATH_NONE ? 0 : 1 + (lp.ksplit > 1);
+  const bool red_here = lp.path == SMLP_PATH_SMALL_M && g_fuse.load() != 2 && lp.sk.blocks / lp.sk.ksplit <= 256;
+  plan->kernels = lp.path == SMLP_PATH_NONE ? 0 : 1 + (lp.ksplit > 1 && !red_here);
   return ok();
 }
 

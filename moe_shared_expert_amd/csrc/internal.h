@@ -72,6 +72,13 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
 // stage configurations it is built for, and the launch with counter slot `slot` and a
 // consumer wait of at most `limit` polls.  Returns a hipError_t.
 constexpr int kLayerSyncSlots = 16;
+// Counter slot of `stream` on the current device (api.cpp; -1 when all are taken), and
+// whether one-launch forms and in-launch reductions are enabled (shared_mlp_tune_layer_fusion).
+int stream_slot(hipStream_t stream);
+bool fusion_enabled();
+// Per-column counters for an in-launch K-split reduction over `columns` columns on
+// `stream`, or null (then a finalize launch reduces) (skinny.hip).
+uint32_t* reduce_counters(hipStream_t stream, int columns);
 bool decode_layer_eligible(const Plan& p);
 int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, const void* w_down, void* out,
                         void* ws, int slot, int limit, hipStream_t s);

@@ -57,6 +57,10 @@ struct SkArgs {
   int fpw;               // LDS kernel: features (gate_up) or rows (down) per workgroup
   int w_rows;            // rows of w
   int ldw;               // elements between consecutive rows of w (>= K)
+  // ksplit > 1: per-column arrival counters (16 words apart, zero between launches) with
+  // which the last-arriving slice of a column sums the partials and applies the epilogue
+  // in the same launch; null: a finalize launch does that.
+  uint32_t* red_cnt;
 };
 
 // Store element (m, n) of h: rne(h) in the first plane and, with two planes, the
@@ -406,11 +410,16 @@ __device__ __forceinline__ void stream_body(const SkArgs& a, char* lds, int col,
       __syncthreads();
     }
   }
-  if (wave != 0) return;
+  // With a K split reduced in this launch, every wave stays for the last-arriving
+  // workgroup's reduction below.
+  const bool reduce_here = ksplit > 1 && a.red_cnt != nullptr;
+  if (wave != 0 && !reduce_here) return;
 
   // Epilogue.  MFMA output: lane (ln, lg), element j = (token mt*16 + 4*lg + j, column ln).
-  // A consumer whose wait gave up writes NaN.
+  // A consumer whose wait gave up writes NaN.  K-split partial sums are stored
+  // agent-coherent when the last-arriving slice reads them in this launch.
   const float poison = ready ? 0.f : __builtin_nanf("");
+  if (wave == 0) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -425,7 +434,9 @@ __device__ __forceinline__ void stream_body(const SkArgs& a, char* lds, int col,
           if (m >= a.M || f >= fend) continue;
           if (ksplit > 1) {
             // lanes 0-7 hold gate columns, lanes 8-15 the matching up columns
-            a.part[((size_t)slice * a.M + m) * (size_t)(2 * a.N) + (ln < 8 ? f : a.N + f)] = v;
+            float* dst = a.part + ((size_t)slice * a.M + m) * (size_t)(2 * a.N) + (ln < 8 ? f : a.N + f);
+            if (reduce_here) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = v;
           } else if (ln < 8) {
             if constexpr (FUSE == FUSE_PRODUCER) store_h_coherent(a.out, a.M, a.N, m, f, silu_mul(v, up));
             else store_h(a.out, a.M, a.N, m, f, silu_mul(v, up), a.h_planes);
@@ -433,14 +444,71 @@ __device__ __forceinline__ void stream_body(const SkArgs& a, char* lds, int col,
         } else {
           const int n = f0 + 16 * t + ln;
           if (m >= a.M || n >= fend) continue;
-          if (ksplit > 1)
-            a.part[((size_t)slice * a.M + m) * (size_t)a.N + n] = v + poison;
-          else if (a.out_f32)
+          if (ksplit > 1) {
+            float* dst = a.part + ((size_t)slice * a.M + m) * (size_t)a.N + n;
+            if (reduce_here) __hip_atomic_store(dst, v + poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = v + poison;
+          } else if (a.out_f32) {
             reinterpret_cast<float*>(a.out)[(size_t)m * a.ldo + n] = v + poison;
-          else
+          } else {
             reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] = (uint16_t)f2bf(v + poison);
+          }
         }
       }
+  }
+  if (!reduce_here) return;
+
+  // In-launch reduction of the K split: once its stores are complete, wave 0 counts this
+  // slice on the column's counter; the last slice to arrive clears the counter and, with
+  // all its waves, sums every slice's partials in slice order (agent-coherent loads; the
+  // same order and arithmetic as the finalize kernel) and applies the epilogue.
+  wait_vmcnt<0>();
+  __syncthreads();
+  int* const last_flag = reinterpret_cast<int*>(lds);  // the rings and the tree are done with
+  if (threadIdx.x == 0) {
+    uint32_t* c = a.red_cnt + 16 * col;
+    const uint32_t prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)ksplit - 1;
+    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *reinterpret_cast<volatile int*>(last_flag) = last;
+  }
+  __syncthreads();
+  if (!*reinterpret_cast<volatile int*>(last_flag)) return;
+  constexpr int P = GU ? 2 : 1;
+  const uint32_t pbytes = (uint32_t)ksplit * (uint32_t)a.M * (uint32_t)(P * a.N) * 4u;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, pbytes);
+  const uint32_t sstride = (uint32_t)a.M * (uint32_t)(P * a.N) * 4u;
+  constexpr int COLS = GU ? 8 * NT : 16 * NT;  // outputs per token row of this workgroup
+  constexpr int SB = 16;                       // slices in flight per batch
+  for (int e = threadIdx.x; e < 16 * MT * COLS; e += WAVES * 64) {
+    const int m = m0 + e / COLS, c = f0 + e % COLS;
+    if (m >= a.M || c >= fend) continue;
+    const uint32_t base = ((uint32_t)m * (uint32_t)(P * a.N) + (uint32_t)c) * 4u;
+    float g = 0.f, u = 0.f;
+    for (int s0 = 0; s0 < ksplit; s0 += SB) {
+      float pg[SB], pu[SB];
+#pragma unroll
+      for (int q = 0; q < SB; ++q)
+        if (s0 + q < ksplit) {
+          const uint32_t o = base + (uint32_t)(s0 + q) * sstride;
+          pg[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)o, 0, 16));
+          if (GU) pu[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)(o + 4u * a.N), 0, 16));
+        }
+#pragma unroll
+      for (int q = 0; q < SB; ++q)
+        if (s0 + q < ksplit) {
+          g += pg[q];
+          if (GU) u += pu[q];
+        }
+    }
+    if (GU) {
+      store_h(a.out, a.M, a.N, m, c, silu_mul(g, u), a.h_planes);
+    } else if (a.out_f32) {
+      reinterpret_cast<float*>(a.out)[(size_t)m * a.ldo + c] = g;
+    } else {
+      reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + c] = (uint16_t)f2bf(g);
+    }
+  }
 }
 
 template <int MT, int NT, int WAVES, int STAGES, int MODE>
@@ -821,9 +889,33 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.fpw = p.gu.fpw;
   a.w_rows = (int)(p.up_off + p.I);
   a.ldw = (int)p.H;
+  a.red_cnt = nullptr;
+  if (p.gu.ksplit > 1 && p.gu.kind == SKINNY_STREAM16)
+    a.red_cnt = reduce_counters(s, p.gu.blocks / (p.gu.ksplit * (p.gu.ttiles > 1 ? p.gu.ttiles : 1)));
   int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
-  if (rc || p.gu.ksplit == 1) return rc;
+  if (rc || p.gu.ksplit == 1 || a.red_cnt) return rc;
   return launch_finalize(true, a.part, p.gu.ksplit, a.M, a.N, a.out, a.N, 0, a.h_planes, s);
+}
+
+// Per-column arrival counters of the in-launch K-split reduction: one block of
+// kRedColumns counters (16 words apart) per stream slot, per device.
+constexpr int kRedColumns = 256;
+__device__ uint32_t g_red_cnt[kLayerSyncSlots * kRedColumns * 16];
+
+uint32_t* reduce_counters(hipStream_t s, int columns) {
+  if (columns > kRedColumns || !fusion_enabled()) return nullptr;
+  const int slot = stream_slot(s);
+  if (slot < 0) return nullptr;
+  static std::mutex mu;
+  static uint32_t* base[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev] && hipGetSymbolAddress((void**)&base[dev], HIP_SYMBOL(g_red_cnt)) != hipSuccess) {
+    base[dev] = nullptr;
+    return nullptr;
+  }
+  return base[dev] + (size_t)slot * kRedColumns * 16;
 }
 
 // Device address of this device's counter slots, looked up once per device.
@@ -874,6 +966,7 @@ int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, con
   g.fpw = p.gu.fpw;
   g.w_rows = (int)(p.up_off + p.I);
   g.ldw = (int)p.H;
+  g.red_cnt = nullptr;
   SkArgs d;
   d.a_hi = reinterpret_cast<const uint16_t*>(static_cast<const char*>(ws) + p.h_offset);
   d.a_lo = nullptr;
@@ -891,6 +984,7 @@ int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, con
   d.fpw = p.dn.fpw;
   d.w_rows = (int)p.H;
   d.ldw = (int)p.ldwd;
+  d.red_cnt = nullptr;
   uint32_t* sync = nullptr;
   const int rc = layer_sync_base(&sync);
   if (rc != (int)hipSuccess) return rc;
@@ -923,8 +1017,10 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.fpw = p.dn.fpw;
   a.w_rows = (int)p.H;
   a.ldw = (int)p.ldwd;
+  a.red_cnt = nullptr;
+  if (p.dn.ksplit > 1 && p.dn.kind == SKINNY_STREAM16) a.red_cnt = reduce_counters(s, p.dn.blocks / p.dn.ksplit);
   int rc = launch_stage<MODE_DOWN_HILO>(p.dn, a, s);
-  if (rc || p.dn.ksplit == 1) return rc;
+  if (rc || p.dn.ksplit == 1 || a.red_cnt) return rc;
   return launch_finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.N, a.out_f32, 1, s);
 }
 
@@ -947,8 +1043,10 @@ int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, voi
   a.fpw = sp.fpw;
   a.w_rows = N;
   a.ldw = ldw > 0 ? ldw : K;
+  a.red_cnt = nullptr;
+  if (sp.ksplit > 1 && sp.kind == SKINNY_STREAM16) a.red_cnt = reduce_counters(s, sp.blocks / sp.ksplit);
   int rc = launch_stage<MODE_LINEAR>(sp, a, s);
-  if (rc || sp.ksplit == 1) return rc;
+  if (rc || sp.ksplit == 1 || a.red_cnt) return rc;
   return launch_finalize(false, part, sp.ksplit, M, N, y, ldy, out_f32, 1, s);
 }
 

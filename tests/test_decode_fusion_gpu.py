@@ -1,12 +1,17 @@
-"""GPU tests of the one-launch decode layer: at M <= 16 the gate_up and down stages of
-shared_mlp_forward run as one grid, the down workgroups waiting (bounded) for the
-gate_up workgroups of the same launch (shared_mlp_tune_layer_fusion).
+"""GPU tests of the one-launch forms.
 
-The fused launch must give the same bits as the two-launch form (same kernels' arithmetic,
-same summation order), stay correct for launches in flight on two streams at once and
-for graph replays, and turn a wait that gives up into NaN output (forced from the host
-with a zero poll limit, so that every kernel still ends normally) without leaving the
-stream's counters unusable for the next call.
+- The decode layer: at M <= 16 the gate_up and down stages of shared_mlp_forward run as
+  one grid, the down workgroups waiting (bounded) for the gate_up workgroups of the same
+  launch.  It must give the same bits as the two-launch form (same arithmetic, same
+  summation order), stay correct for launches in flight on two streams at once and for
+  graph replays, and turn a wait that gives up into NaN output (forced from the host
+  with a zero poll limit, so that every kernel still ends normally) without leaving the
+  stream's counters unusable for the next call.
+- K-split streaming stages (short TP shards at decode sizes, the plain projection):
+  the last-arriving slice of each column sums the partials and applies the epilogue in
+  the same launch; the same bits as the separate finalize launch.
+
+shared_mlp_tune_layer_fusion switches both off (mode 2) for the comparisons.
 """
 import pytest
 import torch
@@ -49,7 +54,7 @@ def forward(x, wgu, wd, partial=False, stream=None, out=None, ws=None):
     if out is None:
         out = torch.full((M, H), float("nan"), dtype=torch.float32 if partial else torch.bfloat16, device=DEV)
     if ws is None:
-        ws = workspace_for(M, H, I, binding.SMLP_BF16)
+        ws = workspace_for(M, H, wd.shape[1], binding.SMLP_BF16)
     binding.shared_mlp_forward(x, wgu, wd, out, partial_fp32=partial, workspace=ws, stream=stream)
     return out
 
@@ -144,3 +149,65 @@ def test_wait_that_gives_up_writes_nan_and_the_stream_recovers(layers):
         good = forward(x, wgu, wd)
         torch.cuda.synchronize()
         assert torch.equal(good, ref)
+
+
+# ------------------------------------------- K-split streaming stages reduced in-launch
+def both_forms(fn):
+    """fn() with the in-launch forms on, then off (separate finalize launches)."""
+    binding.shared_mlp_tune_layer_fusion(1, 0)
+    one = fn()
+    torch.cuda.synchronize()
+    binding.shared_mlp_tune_layer_fusion(2, 0)
+    sep = fn()
+    torch.cuda.synchronize()
+    binding.shared_mlp_tune_layer_fusion(0, 0)
+    return one, sep
+
+
+@pytest.mark.parametrize("M,I_r", [(16, 384), (16, 512), (32, 768), (5, 384)])
+def test_ksplit_gate_up_reduced_in_launch_matches_finalize(M, I_r):
+    # short TP shards at decode sizes: the gate_up stage splits K four ways
+    wgu, wd = synth.layer_weights(H, I_r, config=3, copy=M, fan_in_down=I)
+    g, d = wgu.to(DEV), wd.to(DEV)
+    x = synth.activations(M, H, config=3, copy=M).to(DEV)
+    p = binding.shared_mlp_plan(M, H, I_r, binding.SMLP_BF16, True)
+    assert p["path_name"] == "small_m" and p["gate_up_ksplit"] > 1 and p["kernels"] == 2
+    for rep in range(2):   # the counters are left at zero for the next launch
+        one, sep = both_forms(lambda: forward(x, g, d, partial=True))
+        assert torch.isfinite(one).all()
+        assert torch.equal(one, sep), f"M={M} I_r={I_r} rep {rep}: in-launch reduction differs"
+    ref = oracle.swiglu_mlp(f64(x.cpu()), f64(wgu), f64(wd))
+    assert_rms_close(one, ref, BF16_TOL, f"K-split gate_up reduced in-launch M={M} I_r={I_r}")
+
+
+def test_ksplit_two_plane_down_reduced_in_launch_matches_finalize():
+    M, I_r = 16, 768
+    wgu, wd = synth.layer_weights(H, I_r, config=3, copy=7, fan_in_down=I)
+    g, d = wgu.to(DEV), wd.to(DEV)
+    x = synth.activations(M, H, config=3, copy=7).to(DEV)
+    try:
+        binding.shared_mlp_tune_h_planes(2)
+        binding.shared_mlp_tune_skinny(1, 0, 0, 0, 0, 3)   # down stage split three ways
+        assert binding.shared_mlp_plan(M, H, I_r, binding.SMLP_BF16, True)["down_ksplit"] == 3
+        one, sep = both_forms(lambda: forward(x, g, d, partial=True))
+    finally:
+        binding.shared_mlp_tune_skinny(1, 0, 0, 0, 0, 0)
+        binding.shared_mlp_tune_h_planes(0)
+    assert torch.isfinite(one).all() and torch.equal(one, sep)
+
+
+@pytest.mark.parametrize("N", [132, 264, 2112])
+def test_ksplit_projection_reduced_in_launch_matches_finalize(N):
+    M, K = 16, H
+    w = synth.latent_weight(N, K, copy=N).to(DEV)
+    x = synth.activations(M, K, config=3, copy=N).to(DEV)
+    p = binding.shared_mlp_linear_plan(M, K, N)
+    assert p["down_ksplit"] > 1 and p["kernels"] == 1
+
+    def proj():
+        y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        binding.shared_mlp_linear(x, w, y)
+        return y
+    for rep in range(2):
+        one, sep = both_forms(proj)
+        assert torch.isfinite(one.float()).all() and torch.equal(one, sep), f"N={N} rep {rep}"

@@ -52,7 +52,13 @@ def test_linear_validation_codes(L):
 def test_linear_workspace_rules(L):
     # M = 16 on the streaming kernel splits K: workspace needed, checked, not aliased
     p = binding.shared_mlp_linear_plan(16, K, N)
-    assert p["path_name"] == "small_m" and p["down_ksplit"] > 1 and p["kernels"] == 2
+    # the K split is reduced in the same launch (last-arriving slice per column)...
+    assert p["path_name"] == "small_m" and p["down_ksplit"] > 1 and p["kernels"] == 1
+    try:   # ...or, with in-launch reductions switched off, by a finalize launch
+        binding.shared_mlp_tune_layer_fusion(2, 0)
+        assert binding.shared_mlp_linear_plan(16, K, N)["kernels"] == 2
+    finally:
+        binding.shared_mlp_tune_layer_fusion(0, 0)
     need = binding.shared_mlp_linear_workspace_bytes(16, K, N)
     assert need == p["workspace_bytes"] >= p["down_ksplit"] * 16 * N * 4
     assert _lin(L, n=N, ws=0) == NULL
