@@ -20,7 +20,7 @@ least 200 timed steps in total), each between two HIP events on the launch strea
 a device synchronisation on both sides; the reported time is the median trial.
 ``value`` is the achieved algorithmic HBM bandwidth (weights + x + out bytes per layer
 / time per layer).  ``roofline`` reports the dominant kernel: where the plan runs the
-whole layer as one launch (decode at M <= 16), that kernel, timed by the layer graph
+whole layer as one launch (decode at M <= 32), that kernel, timed by the layer graph
 itself (the gate_up stage alone, from a graph of that stage, is reported beside it);
 otherwise the dominant stage (gate_up + SiLU-and-mul), timed the same way from a graph
 of that stage alone.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of

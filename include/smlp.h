@@ -112,7 +112,7 @@ int shared_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int dtype, size_
  *   partial_fp32 nonzero: write fp32 (a TP rank's partial sum); zero: bf16 output
  *   workspace    device scratch of >= shared_mlp_workspace_bytes(...) bytes, 256-byte
  *                aligned; contents on entry are ignored, on exit unspecified
- * One to five kernels are enqueued on `stream` (see smlp_plan.kernels).  At M <= 16
+ * One to five kernels are enqueued on `stream` (see smlp_plan.kernels).  At M <= 32
  * with bf16 weights the two stages run as one launch whose down workgroups wait
  * (bounded) for the gate_up workgroups of the same launch; it keeps a few counters per
  * stream in a static device array (16 streams per GPU; further streams get the

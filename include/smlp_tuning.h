@@ -63,7 +63,7 @@ int shared_mlp_tune_token_split(int mode);
 int64_t shared_mlp_tune_weight_convert(int64_t min_m);
 
 /* One-launch decode layer: where shared_mlp_forward's plan runs the weight-streaming
- * stages with one plane of h at M <= 16 (the configurations the fused kernel is built
+ * stages with one plane of h at M <= 32 (the configurations the fused kernel is built
  * for), both stages go into one grid: the gate_up workgroups first, then the down
  * workgroups, which take each compute unit as a gate_up workgroup leaves it, issue
  * their first weight loads and wait (bounded) for all of h before loading it.  mode:

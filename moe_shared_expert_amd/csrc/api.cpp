@@ -581,7 +581,7 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
       return sp.ksplit > 1 && !(g_fuse.load() != 2 && sp.kind == smlp::SKINNY_STREAM16 && cols <= 256);
     };
     p->kernels = 2 + finalize_launch(p->gu) + finalize_launch(p->dn);
-    // both stages in one launch (one bf16 plane of h, M <= 16): see shared_mlp_tune_layer_fusion
+    // both stages in one launch (one bf16 plane of h, M <= 32): see shared_mlp_tune_layer_fusion
     if (g_fuse.load() != 2 && smlp::decode_layer_eligible(*p)) p->kernels = 1;
   } else {
     p->path = SMLP_PATH_LARGE_M;

@@ -556,11 +556,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_stream_kernel(SkArgs a) {
 constexpr int kSyncGroups = 16;
 constexpr int kSyncWords = 64 * 35;
 
-template <int MT, int NTG, int SG, int NTD, int SD>
-__global__ __launch_bounds__(512) void decode_layer_kernel(SkArgs gu, SkArgs dn, uint32_t* sync, int producers,
-                                                           int limit) {
+template <int MT, int NTG, int SG, int NTD, int SD, int WD>
+__global__ __launch_bounds__((WD > 4 ? WD : 4) * 64) void decode_layer_kernel(SkArgs gu, SkArgs dn, uint32_t* sync,
+                                                                            int producers, int limit) {
   constexpr int LG = stream_lds_bytes<MT, NTG, 4, SG, MODE_GATE_UP>();
-  constexpr int LD = stream_lds_bytes<MT, NTD, 8, SD, MODE_LINEAR>();
+  constexpr int LD = stream_lds_bytes<MT, NTD, WD, SD, MODE_LINEAR>();
   // The consumer's ready flag sits in a 1 KB pad after the rings: a workgroup LDS size
   // that is not a whole number of KB (a separate 4-byte variable) slowed the streaming
   // loops by ~10% on MI355X (gate_up phase 26.6 -> 29.8 us at M = 16).
@@ -601,7 +601,8 @@ __global__ __launch_bounds__(512) void decode_layer_kernel(SkArgs gu, SkArgs dn,
   uint32_t gen = 0;
   if (threadIdx.x == 0) gen = __hip_atomic_load(gen_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const StreamSync sy{sync + 64 * (17 + c % kSyncGroups), gen + 1u, limit, &flag};
-  stream_body<MT, NTD, 8, SD, MODE_LINEAR, FUSE_CONSUMER>(dn, lds, c, 0, 1, 0, sy);
+  if (threadIdx.x >= WD * 64) return;
+  stream_body<MT, NTD, WD, SD, MODE_LINEAR, FUSE_CONSUMER>(dn, lds, c, 0, 1, 0, sy);
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(sync + 64 * 33, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == consumers - 1) {
@@ -938,12 +939,17 @@ static int layer_sync_base(uint32_t** out) {
   return (int)hipSuccess;
 }
 
+// The stage configurations the one-launch layer is built for: one token tile (gate_up
+// 3 tiles x 4 waves x 3 stages, down 2 tiles x 8 waves x 3 stages) and two token tiles
+// (gate_up 3 x 4 x 3, down 2 x 4 x 4).
 bool decode_layer_eligible(const Plan& p) {
   const SkinnyPlan& g = p.gu;
   const SkinnyPlan& d = p.dn;
-  return p.path == SMLP_PATH_SMALL_M && p.h_dtype == SMLP_BF16 && g.kind == SKINNY_STREAM16 && g.mt == 1 &&
-         g.nb == 3 && g.waves == 4 && g.u == 3 && g.ksplit == 1 && g.ttiles <= 1 && d.kind == SKINNY_STREAM16 &&
-         d.mt == 1 && d.nb == 2 && d.waves == 8 && d.u == 3 && d.ksplit == 1 && g.blocks + d.blocks <= 65535;
+  if (p.path != SMLP_PATH_SMALL_M || p.h_dtype != SMLP_BF16 || g.kind != SKINNY_STREAM16 ||
+      d.kind != SKINNY_STREAM16 || g.ksplit != 1 || d.ksplit != 1 || g.ttiles > 1 || g.mt != d.mt ||
+      g.nb != 3 || g.waves != 4 || g.u != 3 || d.nb != 2 || g.blocks + d.blocks > 65535)
+    return false;
+  return (g.mt == 1 && d.waves == 8 && d.u == 3) || (g.mt == 2 && d.waves == 4 && d.u == 4);
 }
 
 int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, const void* w_down, void* out,
@@ -988,8 +994,12 @@ int launch_decode_layer(const Plan& p, const void* x, const void* w_gate_up, con
   uint32_t* sync = nullptr;
   const int rc = layer_sync_base(&sync);
   if (rc != (int)hipSuccess) return rc;
-  hipLaunchKernelGGL((decode_layer_kernel<1, 3, 3, 2, 3>), dim3(p.gu.blocks + p.dn.blocks), dim3(512), 0, s, g, d,
-                     sync + (size_t)slot * kSyncWords, p.gu.blocks, limit);
+  if (p.gu.mt == 1)
+    hipLaunchKernelGGL((decode_layer_kernel<1, 3, 3, 2, 3, 8>), dim3(p.gu.blocks + p.dn.blocks), dim3(512), 0, s,
+                       g, d, sync + (size_t)slot * kSyncWords, p.gu.blocks, limit);
+  else
+    hipLaunchKernelGGL((decode_layer_kernel<2, 3, 3, 2, 4, 4>), dim3(p.gu.blocks + p.dn.blocks), dim3(256), 0, s,
+                       g, d, sync + (size_t)slot * kSyncWords, p.gu.blocks, limit);
   return (int)hipGetLastError();
 }
 

@@ -372,14 +372,14 @@ def test_ceiling_kernels_validate_before_launch(L):
 
 
 def test_layer_fusion_plan_and_hook(L):
-    """The one-launch decode layer: one kernel for the fused configuration (M <= 16, one
+    """The one-launch decode layer: one kernel for the fused configurations (M <= 32, one
     plane of h, the Kimi-K3 stage tiles), two when it is switched off or does not apply;
     the hook validates its mode before any state changes."""
     try:
-        for M in (1, 8, 16):
+        for M in (1, 8, 16, 17, 32):
             assert binding.shared_mlp_plan(M, H, I)["kernels"] == 1
             assert binding.shared_mlp_plan(M, H, I, BF16, True)["kernels"] == 1
-        assert binding.shared_mlp_plan(32, H, I)["kernels"] == 2      # two token tiles
+        assert binding.shared_mlp_plan(16, 4096, I)["kernels"] == 2   # down tile of another width
         assert binding.shared_mlp_plan(16, H, 128)["kernels"] >= 2     # two planes of h
         binding.shared_mlp_tune_h_planes(2)
         assert binding.shared_mlp_plan(16, H, I)["kernels"] == 2

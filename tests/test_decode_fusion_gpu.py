@@ -1,6 +1,6 @@
 """GPU tests of the one-launch forms.
 
-- The decode layer: at M <= 16 the gate_up and down stages of shared_mlp_forward run as
+- The decode layer: at M <= 32 the gate_up and down stages of shared_mlp_forward run as
   one grid, the down workgroups waiting (bounded) for the gate_up workgroups of the same
   launch.  It must give the same bits as the two-launch form (same arithmetic, same
   summation order), stay correct for launches in flight on two streams at once and for
@@ -60,7 +60,7 @@ def forward(x, wgu, wd, partial=False, stream=None, out=None, ws=None):
 
 
 @pytest.mark.parametrize("partial", [False, True])
-@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
 def test_fused_layer_matches_two_launches_bit_for_bit(M, partial, layers):
     x = synth.activations(M, H, config=2).to(DEV)
     wgu, wd = layers[M % 3]
@@ -81,8 +81,8 @@ def test_fused_layer_matches_two_launches_bit_for_bit(M, partial, layers):
 def test_plan_without_the_fused_configuration_keeps_two_launches():
     # down rows per workgroup differ at H = 4096 (16 instead of 28): two launches
     assert binding.shared_mlp_plan(16, 4096, I, binding.SMLP_BF16, False)["kernels"] == 2
-    # two token tiles (M = 17..32) are not fused either
-    assert binding.shared_mlp_plan(32, H, I, binding.SMLP_BF16, False)["kernels"] == 2
+    # two planes of h (short down contraction) are not fused either
+    assert binding.shared_mlp_plan(32, H, 128, binding.SMLP_BF16, False)["kernels"] >= 2
 
 
 def test_fused_layers_on_two_streams_and_graph_replays(layers):
