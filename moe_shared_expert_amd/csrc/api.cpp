@@ -369,6 +369,17 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     // (M = 2048, I = 6144: 384 tiles, 376 -> 356 us against 128 x 128 tiles).
     gp.bm = 256;
     gp.bn = 256;
+  } else if (!hilo && K >= 4096 && M > 256 && full256 && tiles_for(256, 256) >= 48 &&
+             (stage == 0 ? tiles_for(256, 256) < 384 : tiles_for(256, 256) <= kCUs)) {
+    // Medium M, long K, wide weights: 256 x 256 tiles with the K split that fills about
+    // one round (at most 4 slices; gate_up between one and 1.5 rounds takes 2), against
+    // 256 x 128 and 128 x 128 tiles (graph timings at I = 6144, H = 7168):
+    //   down    M = 384 / 640 / 768 / 896 / 1536 / 1792: 68.0 -> 62.3, 126.1 -> 84.8, 132.5 -> 89.1,
+    //           136.9 -> 107.0, 198.8 -> 185.7, 221.9 -> 192.2 us;
+    //   gate_up M = 512 / 896 / 1024 / 1280 / 1536: 123.6 -> 111.7, 203.3 -> 184.5, 217.5 -> 187.1,
+    //           251.1 -> 196.7, 330.6 -> 316.6 us.
+    gp.bm = 256;
+    gp.bn = 256;
   } else if (!hilo && K >= 4096 && M <= 1024 && full256 &&
              (stage == 0 ? tiles_for(256, 128) >= kCUs / 2 : tiles_for(128, 128) < kCUs)) {
     // Medium M, long K: 256 x 128 tiles (8 waves, 3 stages) with a K split to about three
@@ -453,8 +464,13 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     if (gp.bm == 256 && gp.bn == 128) {
       ks = stage == 0 ? (3 * kCUs + tiles - 1) / tiles : 2;
       if (ks > 4) ks = 4;
-    } else if (gp.bn == 32 || (gp.bm == 256 && gp.bn == 256)) {
-      ks = 1;  // (256 x 256: a down stage from 7/8 of a round takes no K split either)
+    } else if (gp.bm == 256 && gp.bn == 256) {
+      // up to one round of tiles: split K to fill it; gate_up between one and 1.5 rounds:
+      // two slices; else none (a down stage from 7/8 of a round takes no K split either)
+      ks = tiles <= kCUs ? kCUs / tiles : (stage == 0 && tiles < 384) ? 2 : 1;
+      if (ks > 4) ks = 4;
+    } else if (gp.bn == 32) {
+      ks = 1;
     } else if (gp.bn == 64 && gp.bm == 128) {
       // Few weight tiles (medium M): split K until about 3 (gate_up) or 1.75 (down)
       // workgroups per compute unit stream weights; fp32 partials cost 2 M / K of the

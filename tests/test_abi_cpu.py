@@ -117,8 +117,16 @@ def test_default_threshold_and_gemm_tuning(L):
         assert p["down_blocks"] == (M // 256) * (H // 256) and p["down_ksplit"] == 1, (M, p)
     p = binding.shared_mlp_plan(3072, H, I)           # 336 tiles, last round 31% full: split
     assert p["down_blocks"] != 12 * (H // 256) and p["kernels"] == 5, p
-    p = binding.shared_mlp_plan(1536, H, I)           # 168 tiles: 128 x 128 tiles instead
-    assert p["down_blocks"] >= (1536 // 128) * (H // 128), p
+    p = binding.shared_mlp_plan(1536, H, I)           # 168 tiles: one round, no K split
+    assert p["down_blocks"] == (1536 // 256) * (H // 256) and p["down_ksplit"] == 1, p
+    # medium M: 256 x 256 tiles with the K split that fills about one round (at most 4)
+    for M, gks, dks in ((512, 2, 4), (768, 1, 3), (1024, 1, 2), (1280, 1, 1), (1536, 2, 1)):
+        p = binding.shared_mlp_plan(M, H, I)
+        tm = (M + 255) // 256
+        assert (p["gate_up_ksplit"], p["down_ksplit"]) == (gks, dks), (M, p)
+        assert p["gate_up_blocks"] == tm * (2 * I // 256) * gks and p["down_blocks"] == tm * (H // 256) * dks, (M, p)
+    # a TP shard's few weight tiles keep their own rules
+    assert binding.shared_mlp_plan(512, H, I // 8, BF16, True)["gate_up_ksplit"] == 8
     # a pinned down tile is never split
     binding.shared_mlp_tune_gemm(1, bm=256, bn=256, wm=2, wn=4, ns=2)
     try:
