@@ -369,13 +369,20 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     // (M = 2048, I = 6144: 384 tiles, 376 -> 356 us against 128 x 128 tiles).
     gp.bm = 256;
     gp.bn = 256;
-  } else if (!hilo && K >= 4096 && M > 256 && full256 && tiles_for(256, 256) >= 48 &&
+  } else if (!hilo && stage == 0 && K >= 4096 && M > 256 && M <= 384 && !full256 && tiles_for(128, 256) >= 96) {
+    // gate_up at three 128-token tiles (M = 257-384) that would leave 256-token tiles
+    // part empty: 128 x 256 tiles (8 waves, 3 stages) split K three ways, against 128 x
+    // 128 tiles (M = 288 / 320 / 352: 108.2 -> 93.8, 107.9 -> 95.1, 109.0 -> 97.4 us).
+    gp.bm = 128;
+    gp.bn = 256;
+  } else if (!hilo && K >= 4096 && M > 256 && (stage == 1 || full256) && tiles_for(256, 256) >= 48 &&
              (stage == 0 ? tiles_for(256, 256) < 384 : tiles_for(256, 256) <= kCUs)) {
     // Medium M, long K, wide weights: 256 x 256 tiles with the K split that fills about
     // one round (at most 4 slices; gate_up between one and 1.5 rounds takes 2), against
     // 256 x 128 and 128 x 128 tiles (graph timings at I = 6144, H = 7168):
     //   down    M = 384 / 640 / 768 / 896 / 1536 / 1792: 68.0 -> 62.3, 126.1 -> 84.8, 132.5 -> 89.1,
-    //           136.9 -> 107.0, 198.8 -> 185.7, 221.9 -> 192.2 us;
+    //           136.9 -> 107.0, 198.8 -> 185.7, 221.9 -> 192.2 us (also with the second token
+    //           tile part empty: M = 288 / 320 / 352: 68.3 -> 57.6, 69.5 -> 58.3, 70.3 -> 59.6 us);
     //   gate_up M = 512 / 896 / 1024 / 1280 / 1536: 123.6 -> 111.7, 203.3 -> 184.5, 217.5 -> 187.1,
     //           251.1 -> 196.7, 330.6 -> 316.6 us.
     gp.bm = 256;
@@ -441,8 +448,11 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   if (o.ns.load()) {
     gp.ns = o.ns.load();
   } else if (stream_m) {
-    gp.ns = gp.bn == 256 ? 3 : 4;
-  } else if (gp.bm == 256 && gp.bn == 128) {
+    // the down stage's 128 x 128 tiles take two stages (64 KB, two workgroups per compute
+    // unit) and a four-way K split: M = 128 / 192 / 256: 32.8 -> 31.8, 48.0 -> 43.6,
+    // 50.8 -> 47.1 us against four stages and two slices
+    gp.ns = gp.bn == 256 ? 3 : (stage == 1 && gp.bm == 128 && gp.bn == 128) ? 2 : 4;
+  } else if ((gp.bm == 256 && gp.bn == 128) || (gp.bm == 128 && gp.bn == 256)) {
     gp.ns = 3;
   } else {
     // Two stages where compiled (the two-plane 128 x 128 down tile has three).
@@ -459,9 +469,11 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!ks && stream_m && (gp.bm == 64 || (stage == 1 && K < 2048))) {
     ks = 1;
   } else if (!ks && stream_m && gp.bm == 128) {
-    ks = gp.bn == 32 ? 1 : stream_ks(gp.bn);
+    ks = gp.bn == 32 ? 1 : (stage == 1 && gp.bn == 128 && ksteps >= 48) ? 4 : stream_ks(gp.bn);
   } else if (!ks) {
-    if (gp.bm == 256 && gp.bn == 128) {
+    if (gp.bm == 128 && gp.bn == 256) {
+      ks = 3;
+    } else if (gp.bm == 256 && gp.bn == 128) {
       ks = stage == 0 ? (3 * kCUs + tiles - 1) / tiles : 2;
       if (ks > 4) ks = 4;
     } else if (gp.bm == 256 && gp.bn == 256) {
