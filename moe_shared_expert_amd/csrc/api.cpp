@@ -328,6 +328,8 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   // 113 -> 117 us on 256 x 128 tiles, 78% full, while its down stage gained 63.5 -> 61.5).
   const int64_t padded256 = (M + 255) / 256 * 256;
   const bool full256 = stage == 0 ? M * 20 >= 17 * padded256 : M * 4 >= 3 * padded256;
+  bool narrow_gu = false;  // the narrow gate_up rule below, with its own K split
+  bool short_dn = false;   // the short-K down rule below: no K split
   if (o.bm.load() && o.bn.load()) {
     gp.bm = o.bm.load();
     gp.bn = o.bn.load();
@@ -394,6 +396,18 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     // 131.7 -> 122.0 us, down 73.0 -> 63.0 us; M = 1024: gate_up 237 -> 207 us.
     gp.bm = 256;
     gp.bn = 128;
+  } else if (!hilo && stage == 0 && K >= 4096 && M > 256 && tiles_for(128, 128) < kCUs) {
+    // Narrow gate_up (the I of a TP shard) at medium M: 8-wave tiles with K split to about
+    // 432 workgroups (two per compute unit), 128 x 64 (3 stages) up to 48 tiles of
+    // 128 x 128, else 128 x 128 (2 stages), against 4-wave 128 x 64 tiles split to about
+    // three per compute unit (TP8 M = 384 / 768 / 1536: 29.5 -> 23.0, 39.5 -> 31.3,
+    // 65.7 -> 48.4 us; TP16 M = 384 / 1536 / 3072: 22.0 -> 17.5, 39.6 -> 31.2,
+    // 65.6 -> 48.2 us).
+    gp.bn = tiles_for(128, 128) <= 48 ? 64 : 128;
+    gp.bm = 128;
+    gp.wm = 4;
+    gp.wn = 2;
+    narrow_gu = true;
   } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs) ||
              (stage == 1 && !hilo && K >= 2048 && tiles_for(128, 128) >= kCUs / 2)) {
     // The long-K down stage also takes 128 x 128 tiles from half a tile per compute
@@ -406,6 +420,18 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     // split, so no fp32 partials and no finalize pass (half the time at M = 128).
     gp.bm = 128;
     gp.bn = 32;
+  } else if (stage == 1 && !hilo && K < 2048 && M > 256) {
+    // Short-K down below one round of 128 x 128 tiles at two per compute unit: those
+    // tiles from 3/4 of that round, else 128 x 64 tiles on 8 waves (3 stages), against
+    // 4-wave 128 x 64 tiles (TP8 M = 512 / 768 / 1024: 14.8 -> 13.2, 19.7 -> 18.8,
+    // 27.1 -> 21.1 us; TP16 11.2 -> 9.7, 13.8 -> 13.1, 19.5 -> 15.4 us).  No K split:
+    // with a contraction this short the fp32 partials and their finalize pass cost as much
+    // as the GEMM (TP8 M = 320: 21.5 us with two slices, 11.7 us with one).
+    gp.bm = 128;
+    gp.bn = tiles_for(128, 128) * 4 >= 3 * 2 * kCUs ? 128 : 64;
+    gp.wm = 4;
+    gp.wn = 2;
+    short_dn = true;
   } else {
     gp.bm = 128;
     gp.bn = 64;
@@ -471,7 +497,12 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!ks && stream_m && gp.bm == 128) {
     ks = gp.bn == 32 ? 1 : (stage == 1 && gp.bn == 128 && ksteps >= 48) ? 4 : stream_ks(gp.bn);
   } else if (!ks) {
-    if (gp.bm == 128 && gp.bn == 256) {
+    if (narrow_gu) {
+      ks = 432 / tiles;
+      if (ks > 6) ks = 6;
+    } else if (short_dn) {
+      ks = 1;
+    } else if (gp.bm == 128 && gp.bn == 256) {
       ks = 3;
     } else if (gp.bm == 256 && gp.bn == 128) {
       ks = stage == 0 ? (3 * kCUs + tiles - 1) / tiles : 2;

@@ -125,8 +125,15 @@ def test_default_threshold_and_gemm_tuning(L):
         tm = (M + 255) // 256
         assert (p["gate_up_ksplit"], p["down_ksplit"]) == (gks, dks), (M, p)
         assert p["gate_up_blocks"] == tm * (2 * I // 256) * gks and p["down_blocks"] == tm * (H // 256) * dks, (M, p)
-    # a TP shard's few weight tiles keep their own rules
-    assert binding.shared_mlp_plan(512, H, I // 8, BF16, True)["gate_up_ksplit"] == 8
+    # a TP shard's few weight tiles keep their own rules: gate_up on 8-wave tiles split to
+    # about 432 workgroups (128 x 64 up to 48 tiles of 128 x 128, at most 6 slices), the
+    # short-K down stage never split
+    for tp, M, bn, gks, dbn in ((8, 320, 64, 6, 64), (8, 512, 64, 4, 64), (8, 768, 128, 6, 64),
+                                (8, 1024, 128, 4, 128), (8, 1536, 128, 3, 128), (16, 1536, 128, 6, 128)):
+        p = binding.shared_mlp_plan(M, H, I // tp, BF16, True)
+        tm = (M + 127) // 128
+        assert p["gate_up_ksplit"] == gks and p["gate_up_blocks"] == tm * (2 * I // tp // bn) * gks, (tp, M, p)
+        assert p["down_ksplit"] == 1 and p["down_blocks"] == tm * (H // dbn) and p["kernels"] == 3, (tp, M, p)
     # a pinned down tile is never split
     binding.shared_mlp_tune_gemm(1, bm=256, bn=256, wm=2, wn=4, ns=2)
     try:

@@ -330,15 +330,18 @@ def test_sweep_replicated(M, full_layer):
     assert_rms_close(out, ref, BF16_TOL, f"sweep rep M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 2048])
-def test_sweep_tp8(M, full_layer):
+@pytest.mark.parametrize("tp,M", [(8, 1), (8, 8), (8, 32), (8, 128), (8, 320), (8, 512), (8, 1000), (8, 1536),
+                                  (8, 2048), (16, 384), (16, 1536)])
+def test_sweep_tp(tp, M, full_layer):
+    # rank 5's shard; M = 320 ... 1536 run the narrow 8-wave gate_up tiles split about
+    # 432 ways and the unsplit short-K down tiles, 320 and 1000 with a ragged token tile
     wgu, wd, wgu64, wd64 = full_layer
-    g_r, d_r = oracle.rank_shard(wgu64, wd64, 8, 5)
-    x = synth.activations(M, H, config=5, copy=10000 + M)
-    wgu_r, wd_r = slice_on_gpu(wgu.to(DEV), wd.to(DEV), 8, 5)
+    g_r, d_r = oracle.rank_shard(wgu64, wd64, tp, 5)
+    x = synth.activations(M, H, config=5, copy=10000 * tp + M)
+    wgu_r, wd_r = slice_on_gpu(wgu.to(DEV), wd.to(DEV), tp, 5)
     out = run_forward(x.to(DEV), wgu_r, wd_r, partial=True)
     ref = oracle.swiglu_mlp(f64(x), g_r, d_r)
-    assert_rms_close(out, ref, BF16_TOL, f"sweep tp8 M={M}")
+    assert_rms_close(out, ref, BF16_TOL, f"sweep tp{tp} M={M}")
 
 
 # ------------------------------------------------------------------ edge cases
