@@ -764,7 +764,8 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
                                                        int ldo, int out_f32, int h_fmt) {
   // Four consecutive features per thread (N % 4 == 0): 16-byte partial loads, up to
   // sixteen slices in flight at a time, summed in slice order.  Down and projection outputs
-  // have row stride ldo (a multiple of 4).
+  // have row stride ldo (a multiple of 4).  The partials (read once) are loaded and an fp32
+  // output stored non-temporally, as the tiled kernel stores them.
   constexpr int P = GU ? 2 : 1;
   const int N4 = N >> 2;
   const size_t total = (size_t)M * N4;
@@ -782,8 +783,8 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
 #pragma unroll
       for (int q = 0; q < SB; ++q) {
         if (s + q < ksplit) {
-          a[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride);
-          if (GU) b[q] = *reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride + N);
+          a[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride));
+          if (GU) b[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + (size_t)(s + q) * sstride + N));
         }
       }
 #pragma unroll
@@ -813,7 +814,7 @@ __global__ __launch_bounds__(256) void skinny_finalize(const float* __restrict__
       if (h_fmt == 2)
         *reinterpret_cast<u32x2*>(hp + (size_t)M * N + o) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     } else if (out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = g;
+      __builtin_nontemporal_store(g, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o));
     } else {
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + o) =
           u32x2{f2bf(g[0]) | (f2bf(g[1]) << 16), f2bf(g[2]) | (f2bf(g[3]) << 16)};
