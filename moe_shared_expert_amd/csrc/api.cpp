@@ -533,6 +533,11 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   const int64_t kslice = ((K + ks - 1) / ks + 63) / 64 * 64;
   gp.ksplit = (int)((K + kslice - 1) / kslice);
   gp.kslice = (int)kslice;
+  // Non-temporal weight loads where every workgroup streams its weights exactly once and
+  // all re-read the activations: one token tile, long K, wide weights (the replicated
+  // layer at M <= 128; TP shards, with short K or few weight rows, were slower with it).
+  gp.ntb = !hilo && gp.tiles_m == 1 && K >= 2048 && N * fpr >= 4096 &&
+           smlp::gemm_nt_instantiated(hilo, gp.bm, gp.bn, gp.wm, gp.wn, gp.ns);
   *out = gp;
   return true;
 }

@@ -41,6 +41,12 @@ namespace {
 
 
 enum { GM_GATE_UP = 0, GM_DOWN_BF16 = 1, GM_DOWN_HILO = 2, GM_DOWN_F16 = 3, GM_DOWN_F16W = 4 };
+// Mode flag: weight (B) loads carry the non-temporal bit.  Where every workgroup streams
+// its weights exactly once (one token tile, long K, wide weights: the replicated layer at
+// M <= 128) this keeps them from displacing the activations that all workgroups re-read
+// (replicated gate_up at M = 40 / 64 / 128: 40.2 -> 37.1-38.4, 43.2 -> 39.2-40.8,
+// 49.1 -> 45.7 us).  TP shards (short K) and larger M were slower with it.
+constexpr int GM_NTB = 8;
 
 struct GArgs {
   const uint16_t* a;      // [M, K] bf16 (down, two planes: hi)
@@ -132,10 +138,12 @@ __device__ __forceinline__ void wait_steps(int later) {
 
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
-  constexpr bool GU = MODE == GM_GATE_UP;
-  constexpr bool F16 = MODE == GM_DOWN_F16;      // fp16 h, bf16 weights converted in registers
-  constexpr bool F16W = MODE == GM_DOWN_F16W;    // fp16 h, fp16 weights (converted beforehand)
-  constexpr int NA = MODE == GM_DOWN_HILO ? 2 : 1;
+  constexpr int BASE = MODE & 7;
+  constexpr bool NTB = (MODE & GM_NTB) != 0;
+  constexpr bool GU = BASE == GM_GATE_UP;
+  constexpr bool F16 = BASE == GM_DOWN_F16;      // fp16 h, bf16 weights converted in registers
+  constexpr bool F16W = BASE == GM_DOWN_F16W;    // fp16 h, fp16 weights (converted beforehand)
+  constexpr int NA = BASE == GM_DOWN_HILO ? 2 : 1;
   constexpr int W = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
   constexpr int AL = BM / 8 / W, BL = BN / 8 / W;      // 1 KB block loads per wave per step
@@ -214,7 +222,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
     } else {
       const int i = l - NA * AL;
       const bool ok = boff[i] != bbytes && k0 + bchk[i] * 8 < kend;
-      buf_ld_lds(brsc, st + NA * A_BYTES + (i * W + wave) * 1024, ok ? boff[i] + kb : bbytes);
+      if constexpr (NTB) buf_ld_lds_nt(brsc, st + NA * A_BYTES + (i * W + wave) * 1024, ok ? boff[i] + kb : bbytes);
+      else buf_ld_lds(brsc, st + NA * A_BYTES + (i * W + wave) * 1024, ok ? boff[i] + kb : bbytes);
     }
   };
   auto issue = [&](int buf, int k0) {
@@ -453,12 +462,19 @@ int launch_mode(const GemmPlan& gp, const GArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gemm_kernel<BM_, BN_, WM_, WN_, NS_, MODE>), grid, dim3(WM_ * WN_ * 64), 0, s, a); \
     return (int)hipGetLastError();                                                               \
   }
-  if constexpr (MODE == GM_DOWN_HILO) {
-    SMLP_GEMM_HILO_CONFIGS(SMLP_G)
+  if constexpr ((MODE & GM_NTB) != 0) {
+    SMLP_GEMM_NT_CONFIGS(SMLP_G)
   } else {
-    SMLP_GEMM_CONFIGS(SMLP_G)
-    if constexpr (MODE == GM_DOWN_BF16 || MODE == GM_DOWN_F16 || MODE == GM_DOWN_F16W) {
-      SMLP_GEMM_DN_CONFIGS(SMLP_G)
+    if constexpr (MODE != GM_DOWN_HILO && MODE != GM_DOWN_F16W) {
+      if (gp.ntb) return launch_mode<MODE | GM_NTB>(gp, a, s);
+    }
+    if constexpr (MODE == GM_DOWN_HILO) {
+      SMLP_GEMM_HILO_CONFIGS(SMLP_G)
+    } else {
+      SMLP_GEMM_CONFIGS(SMLP_G)
+      if constexpr (MODE == GM_DOWN_BF16 || MODE == GM_DOWN_F16 || MODE == GM_DOWN_F16W) {
+        SMLP_GEMM_DN_CONFIGS(SMLP_G)
+      }
     }
   }
 #undef SMLP_G

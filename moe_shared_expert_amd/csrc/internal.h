@@ -35,6 +35,7 @@ struct GemmPlan {
   int tiles;
   int ksplit;    // workgroups along K
   int kslice;    // K elements per slice (multiple of 64)
+  int ntb;       // weight loads non-temporal (a tile of SMLP_GEMM_NT_CONFIGS)
 };
 
 struct Plan {

@@ -55,7 +55,21 @@ inline bool skinny_instantiated(int stage, int kind, int mt, int nb, int waves, 
 // Down only (one MFMA tile column per wave cannot pair gate and up rows).
 #define SMLP_GEMM_DN_CONFIGS(X) X(128, 32, 4, 1, 2) X(128, 32, 4, 1, 4)
 #define SMLP_GEMM_HILO_CONFIGS(X) X(128, 128, 2, 2, 3) X(128, 64, 4, 1, 2) X(128, 64, 4, 1, 4)
+// Tiles also built with non-temporal weight loads (one bf16 plane or fp16 h only), for
+// plans whose weights every workgroup streams exactly once: one token tile, long K, wide
+// weights (the replicated layer at M <= 128).
+#define SMLP_GEMM_NT_CONFIGS(X) X(128, 256, 2, 4, 3) X(128, 128, 4, 2, 2)
 
+
+inline bool gemm_nt_instantiated(bool hilo, int bm, int bn, int wm, int wn, int ns) {
+#define SMLP_GM(BM_, BN_, WM_, WN_, NS_) \
+  if (bm == BM_ && bn == BN_ && wm == WM_ && wn == WN_ && ns == NS_) return true;
+  if (!hilo) {
+    SMLP_GEMM_NT_CONFIGS(SMLP_GM)
+  }
+#undef SMLP_GM
+  return false;
+}
 
 inline bool gemm_instantiated(int stage, bool hilo, int bm, int bn, int wm, int wn, int ns) {
 #define SMLP_GM(BM_, BN_, WM_, WN_, NS_) \

@@ -321,7 +321,7 @@ def test_gate_up_column_split_ragged():
 
 
 # ---------------------------------------------- M sweep, replicated and TP8 shard
-@pytest.mark.parametrize("M", [1, 8, 32, 128, 512, 768, 1280, 2048])
+@pytest.mark.parametrize("M", [1, 8, 32, 40, 96, 128, 512, 768, 1280, 2048])
 def test_sweep_replicated(M, full_layer):
     wgu, wd, wgu64, wd64 = full_layer
     x = synth.activations(M, H, config=5, copy=M)
