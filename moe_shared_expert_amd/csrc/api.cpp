@@ -397,16 +397,22 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     gp.bm = 256;
     gp.bn = 128;
   } else if (!hilo && stage == 0 && K >= 4096 && M > 256 && tiles_for(128, 128) < kCUs) {
-    // Narrow gate_up (the I of a TP shard) at medium M: 8-wave tiles with K split to about
-    // 432 workgroups (two per compute unit), 128 x 64 (3 stages) up to 48 tiles of
-    // 128 x 128, else 128 x 128 (2 stages), against 4-wave 128 x 64 tiles split to about
-    // three per compute unit (TP8 M = 384 / 768 / 1536: 29.5 -> 23.0, 39.5 -> 31.3,
-    // 65.7 -> 48.4 us; TP16 M = 384 / 1536 / 3072: 22.0 -> 17.5, 39.6 -> 31.2,
-    // 65.6 -> 48.2 us).
-    gp.bn = tiles_for(128, 128) <= 48 ? 64 : 128;
+    // Narrow gate_up (the I of a TP shard) at medium M streams weights that no cache
+    // holds across a stack of layers, as the M <= 256 plans do: 128 x 256 tiles (8 waves,
+    // 3 stages, one workgroup per compute unit) with K split to about 224 workgroups (at
+    // most 12 slices), or, under 16 such tiles, 128 x 64 tiles on 8 waves split to about
+    // 192.  Measured with 24 (TP8) or 48 (TP16) distinct weight copies, so that the weights
+    // come from HBM, against 4-wave 128 x 64 tiles split to about 768 workgroups: TP8 M =
+    // 512 / 1024 / 1536 35.1 -> 26.3, 45.8 -> 37.0, 52.1 -> 49.7 us; TP16 M = 512 / 1024 /
+    // 2048 25.4 -> 20.1, 33.4 -> 26.3, 44.4 -> 37.4 us.
     gp.bm = 128;
-    gp.wm = 4;
-    gp.wn = 2;
+    if (tiles_for(128, 256) >= 16) {
+      gp.bn = 256;
+    } else {
+      gp.bn = 64;
+      gp.wm = 4;
+      gp.wn = 2;
+    }
     narrow_gu = true;
   } else if (tiles_for(128, 128) >= (stage == 0 ? kCUs : 2 * kCUs) ||
              (stage == 1 && !hilo && K >= 2048 && tiles_for(128, 128) >= kCUs / 2)) {
@@ -421,14 +427,15 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
     gp.bm = 128;
     gp.bn = 32;
   } else if (stage == 1 && !hilo && K < 2048 && M > 256) {
-    // Short-K down below one round of 128 x 128 tiles at two per compute unit: those
-    // tiles from 3/4 of that round, else 128 x 64 tiles on 8 waves (3 stages), against
-    // 4-wave 128 x 64 tiles (TP8 M = 512 / 768 / 1024: 14.8 -> 13.2, 19.7 -> 18.8,
-    // 27.1 -> 21.1 us; TP16 11.2 -> 9.7, 13.8 -> 13.1, 19.5 -> 15.4 us).  No K split:
-    // with a contraction this short the fp32 partials and their finalize pass cost as much
-    // as the GEMM (TP8 M = 320: 21.5 us with two slices, 11.7 us with one).
+    // Short-K down below two rounds of 128 x 128 tiles: those tiles (8 waves, 2 stages)
+    // once there are more of them than compute units, else 128 x 64 tiles on 8 waves
+    // (3 stages); weights from HBM (24 / 48 distinct copies), against 4-wave 128 x 64
+    // tiles: TP8 M = 384 / 640 / 768 24.3 -> 15.2, 21.3 -> 19.1, 22.5 -> 20.7 us; TP16
+    // 18.2 -> 10.2, 13.9 -> 13.0, 14.0 -> 14.2 us.  No K split: with a contraction this
+    // short the fp32 partials and their finalize pass cost as much as the GEMM (TP8
+    // M = 320: 21.5 us with two slices, 11.7 us with one).
     gp.bm = 128;
-    gp.bn = tiles_for(128, 128) * 4 >= 3 * 2 * kCUs ? 128 : 64;
+    gp.bn = tiles_for(128, 128) > kCUs ? 128 : 64;
     gp.wm = 4;
     gp.wn = 2;
     short_dn = true;
@@ -497,8 +504,11 @@ bool plan_gemm(int stage, int64_t M, int64_t N, int64_t K, bool hilo, smlp::Gemm
   } else if (!ks && stream_m && gp.bm == 128) {
     ks = gp.bn == 32 ? 1 : (stage == 1 && gp.bn == 128 && ksteps >= 48) ? 4 : stream_ks(gp.bn);
   } else if (!ks) {
-    if (narrow_gu) {
-      ks = 432 / tiles;
+    if (narrow_gu && gp.bn == 256) {
+      ks = 224 / tiles;
+      if (ks > 12) ks = 12;
+    } else if (narrow_gu) {
+      ks = (192 + tiles - 1) / tiles;
       if (ks > 6) ks = 6;
     } else if (short_dn) {
       ks = 1;

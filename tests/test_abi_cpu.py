@@ -125,11 +125,13 @@ def test_default_threshold_and_gemm_tuning(L):
         tm = (M + 255) // 256
         assert (p["gate_up_ksplit"], p["down_ksplit"]) == (gks, dks), (M, p)
         assert p["gate_up_blocks"] == tm * (2 * I // 256) * gks and p["down_blocks"] == tm * (H // 256) * dks, (M, p)
-    # a TP shard's few weight tiles keep their own rules: gate_up on 8-wave tiles split to
-    # about 432 workgroups (128 x 64 up to 48 tiles of 128 x 128, at most 6 slices), the
-    # short-K down stage never split
-    for tp, M, bn, gks, dbn in ((8, 320, 64, 6, 64), (8, 512, 64, 4, 64), (8, 768, 128, 6, 64),
-                                (8, 1024, 128, 4, 128), (8, 1536, 128, 3, 128), (16, 1536, 128, 6, 128)):
+    # a TP shard's few weight tiles keep their own rules: gate_up on 128 x 256 tiles split to
+    # about 224 workgroups (at most 12 slices), or under 16 such tiles on 8-wave 128 x 64
+    # tiles split to about 192 (at most 6); the short-K down stage never split, 128 x 128
+    # tiles once they outnumber the compute units, else 128 x 64
+    for tp, M, bn, gks, dbn in ((8, 320, 256, 12, 64), (8, 512, 256, 9, 64), (8, 640, 256, 7, 128),
+                                (8, 1024, 256, 4, 128), (8, 1536, 256, 3, 128), (16, 384, 64, 6, 64),
+                                (16, 512, 64, 4, 64), (16, 1024, 256, 9, 128), (16, 2048, 256, 4, 128)):
         p = binding.shared_mlp_plan(M, H, I // tp, BF16, True)
         tm = (M + 127) // 128
         assert p["gate_up_ksplit"] == gks and p["gate_up_blocks"] == tm * (2 * I // tp // bn) * gks, (tp, M, p)

@@ -330,11 +330,12 @@ def test_sweep_replicated(M, full_layer):
     assert_rms_close(out, ref, BF16_TOL, f"sweep rep M={M}")
 
 
-@pytest.mark.parametrize("tp,M", [(8, 1), (8, 8), (8, 32), (8, 128), (8, 320), (8, 512), (8, 1000), (8, 1536),
-                                  (8, 2048), (16, 384), (16, 1536)])
+@pytest.mark.parametrize("tp,M", [(8, 1), (8, 8), (8, 32), (8, 128), (8, 320), (8, 512), (8, 640), (8, 1000),
+                                  (8, 1536), (8, 2048), (16, 384), (16, 1024), (16, 1536)])
 def test_sweep_tp(tp, M, full_layer):
-    # rank 5's shard; M = 320 ... 1536 run the narrow 8-wave gate_up tiles split about
-    # 432 ways and the unsplit short-K down tiles, 320 and 1000 with a ragged token tile
+    # rank 5's shard; M = 320 ... 1536 run the narrow gate_up plans (128 x 256 tiles split
+    # 3-12 ways, or 8-wave 128 x 64 tiles) and the unsplit short-K down tiles (128 x 64 or
+    # 128 x 128), 320 and 1000 with a ragged token tile
     wgu, wd, wgu64, wd64 = full_layer
     g_r, d_r = oracle.rank_shard(wgu64, wd64, tp, 5)
     x = synth.activations(M, H, config=5, copy=10000 * tp + M)
