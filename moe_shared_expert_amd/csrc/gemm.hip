@@ -394,9 +394,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GArgs g) {
 
   // Epilogue.  32x32 output: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
   // K-split partials (read once, by the finalize) and the down output (read once, by the
-  // caller) are stored non-temporally: TP8 / TP16 layers at M = 128 22.2 -> 21.7 and
-  // 18.9 -> 18.0 us, at M = 256 28.5 -> 26.7 and 22.3 -> 20.4 us, with the finalize's
-  // partial loads non-temporal too.  h stays a normal store (the down stage re-reads it).
+  // caller) are stored non-temporally, and the finalize loads the partials non-temporally:
+  // with weights from HBM, TP16 layers at M = 64 / 128 / 256 18.4 -> 17.7, 19.3 -> 18.1,
+  // 23.1 -> 21.2 us, TP8 at M = 256 30.9 -> 29.0 us, replicated at M = 64 / 512 81 -> 75,
+  // 213 -> 202 us.  h stays a normal store (the down stage re-reads it).
   // gate_up: MFMA tile j holds gate features and tile j + TN/2 the matching up rows; with
   // one MFMA tile column per wave (TN = 1) its columns 0-15 are gate features and 16-31
   // the matching up rows, brought together by exchanging lanes l and l ^ 16.
