@@ -230,6 +230,11 @@ bool plan_skinny(int stage, int64_t M, int64_t N, int64_t K, smlp::SkinnyPlan* o
     sp.fpw = 0;
   }
   if (!smlp::skinny_instantiated(inst, sp.kind, sp.mt, sp.nb, sp.waves, sp.u)) return false;
+  // The in-launch K-split reduction is used with the planner's own shapes only (a pinned
+  // K split alone keeps it); a pinned tile count, wave count or ring depth takes the
+  // finalize launch.  A sweep of pinned streaming shapes with K splits (8 waves, 1-4
+  // tiles, 3-4 stages) ended in a GPU memory fault whose cause was not found.
+  sp.red_ok = !o.nb.load() && !o.waves.load() && !o.u.load();
   *out = sp;
   return true;
 }
@@ -652,7 +657,7 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     // column applies the epilogue) when there are at most 256 columns; else a finalize launch
     auto finalize_launch = [](const smlp::SkinnyPlan& sp) {
       const int cols = sp.blocks / (sp.ksplit * (sp.ttiles > 1 ? sp.ttiles : 1));
-      return sp.ksplit > 1 && !(g_fuse.load() != 2 && sp.kind == smlp::SKINNY_STREAM16 && cols <= 256);
+      return sp.ksplit > 1 && !(g_fuse.load() != 2 && sp.kind == smlp::SKINNY_STREAM16 && sp.red_ok && cols <= 256);
     };
     p->kernels = 2 + finalize_launch(p->gu) + finalize_launch(p->dn);
     // both stages in one launch (one bf16 plane of h, M <= 32): see shared_mlp_tune_layer_fusion
@@ -782,6 +787,7 @@ int make_linear_plan(int64_t M, int64_t K, int64_t N, int64_t ldy, LinearPlan* l
     sp.ksplit = (int)ks;
     sp.kslice = (int)kslice;
     sp.blocks = (int)(groups * ks);
+    sp.red_ok = !o.nb.load() && !o.waves.load() && !o.u.load();  // as for the layer stages
     lp->path = SMLP_PATH_SMALL_M;
     lp->ksplit = sp.ksplit;
     lp->blocks = sp.blocks;
@@ -1030,7 +1036,8 @@ int shared_mlp_linear_plan(int64_t M, int64_t K, int64_t N, smlp_plan* plan) {
   plan->workspace_bytes = lp.part_bytes;
   plan->down_ksplit = lp.path == SMLP_PATH_NONE ? 1 : lp.ksplit;
   plan->down_blocks = lp.blocks;
-  const bool red_here = lp.path == SMLP_PATH_SMALL_M && g_fuse.load() != 2 && lp.sk.blocks / lp.sk.ksplit <= 256;
+  const bool red_here = lp.path == SMLP_PATH_SMALL_M && g_fuse.load() != 2 && lp.sk.red_ok &&
+                        lp.sk.blocks / lp.sk.ksplit <= 256;
   plan->kernels = lp.path == SMLP_PATH_NONE ? 0 : 1 + (lp.ksplit > 1 && !red_here);
   return ok();
 }

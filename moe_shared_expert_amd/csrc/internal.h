@@ -22,6 +22,7 @@ struct SkinnyPlan {
   int fpw;       // SKINNY_STREAM16: features (gate_up) or rows (down) per workgroup
   int ttiles;    // SKINNY_STREAM16 token split: workgroups along M, 16 * mt tokens each
                  // (0 or 1 = none; blocks counts every workgroup)
+  int red_ok;    // a K split may be reduced in the same launch (off for a pinned shape)
 };
 
 enum { SKINNY_DIRECT16 = 2, SKINNY_STREAM16 = 3 };

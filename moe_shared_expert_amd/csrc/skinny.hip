@@ -892,7 +892,7 @@ int launch_skinny_gate_up(const Plan& p, const void* x, const void* w_gate_up, v
   a.w_rows = (int)(p.up_off + p.I);
   a.ldw = (int)p.H;
   a.red_cnt = nullptr;
-  if (p.gu.ksplit > 1 && p.gu.kind == SKINNY_STREAM16)
+  if (p.gu.ksplit > 1 && p.gu.kind == SKINNY_STREAM16 && p.gu.red_ok)
     a.red_cnt = reduce_counters(s, p.gu.blocks / (p.gu.ksplit * (p.gu.ttiles > 1 ? p.gu.ttiles : 1)));
   int rc = launch_stage<MODE_GATE_UP>(p.gu, a, s);
   if (rc || p.gu.ksplit == 1 || a.red_cnt) return rc;
@@ -1029,7 +1029,8 @@ int launch_skinny_down(const Plan& p, const void* w_down, void* out, void* ws, h
   a.w_rows = (int)p.H;
   a.ldw = (int)p.ldwd;
   a.red_cnt = nullptr;
-  if (p.dn.ksplit > 1 && p.dn.kind == SKINNY_STREAM16) a.red_cnt = reduce_counters(s, p.dn.blocks / p.dn.ksplit);
+  if (p.dn.ksplit > 1 && p.dn.kind == SKINNY_STREAM16 && p.dn.red_ok)
+    a.red_cnt = reduce_counters(s, p.dn.blocks / p.dn.ksplit);
   int rc = launch_stage<MODE_DOWN_HILO>(p.dn, a, s);
   if (rc || p.dn.ksplit == 1 || a.red_cnt) return rc;
   return launch_finalize(false, a.part, p.dn.ksplit, a.M, a.N, out, a.N, a.out_f32, 1, s);
@@ -1055,7 +1056,7 @@ int launch_skinny_linear(const SkinnyPlan& sp, const void* x, const void* w, voi
   a.w_rows = N;
   a.ldw = ldw > 0 ? ldw : K;
   a.red_cnt = nullptr;
-  if (sp.ksplit > 1 && sp.kind == SKINNY_STREAM16) a.red_cnt = reduce_counters(s, sp.blocks / sp.ksplit);
+  if (sp.ksplit > 1 && sp.kind == SKINNY_STREAM16 && sp.red_ok) a.red_cnt = reduce_counters(s, sp.blocks / sp.ksplit);
   int rc = launch_stage<MODE_LINEAR>(sp, a, s);
   if (rc || sp.ksplit == 1 || a.red_cnt) return rc;
   return launch_finalize(false, part, sp.ksplit, M, N, y, ldy, out_f32, 1, s);

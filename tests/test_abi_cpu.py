@@ -411,3 +411,27 @@ def test_layer_fusion_plan_and_hook(L):
     finally:
         binding.shared_mlp_tune_h_planes(0)
         binding.shared_mlp_tune_layer_fusion(0, 0)
+
+
+def test_pinned_streaming_shape_takes_the_finalize_launch(L):
+    """A K-split streaming stage is reduced in its own launch with the planner's shapes or a
+    pinned K split alone; a pinned tile count, wave count or ring depth takes the finalize
+    launch (one more kernel), for the layer stages and the projection alike."""
+    I16 = I // 16   # a TP16 shard: the default gate_up splits K four ways at M = 16
+    try:
+        base = binding.shared_mlp_plan(16, H, I16, BF16, True)
+        assert base["gate_up_ksplit"] > 1 and base["kernels"] == 2
+        binding.shared_mlp_tune_skinny(0, ksplit=3)
+        assert binding.shared_mlp_plan(16, H, I16, BF16, True)["kernels"] == 2
+        for pin in (dict(kind=3, nb=2), dict(kind=3, waves=8), dict(kind=3, nb=3, u=5)):
+            binding.shared_mlp_tune_skinny(0, ksplit=3, **pin)
+            p = binding.shared_mlp_plan(16, H, I16, BF16, True)
+            assert p["gate_up_ksplit"] == 3 and p["kernels"] == 3, (pin, p)
+        binding.shared_mlp_tune_skinny(0)
+        binding.shared_mlp_tune_skinny(2, ksplit=4)
+        assert binding.shared_mlp_linear_plan(16, H, 2112)["kernels"] == 1
+        binding.shared_mlp_tune_skinny(2, kind=3, nb=2, waves=4, u=4, ksplit=4)
+        assert binding.shared_mlp_linear_plan(16, H, 2112)["kernels"] == 2
+    finally:
+        binding.shared_mlp_tune_skinny(0)
+        binding.shared_mlp_tune_skinny(2)
