@@ -331,15 +331,16 @@ def test_sweep_replicated(M, full_layer):
 
 
 @pytest.mark.parametrize("tp,M", [(8, 1), (8, 8), (8, 32), (8, 128), (8, 320), (8, 512), (8, 640), (8, 1000),
-                                  (8, 1536), (8, 2048), (16, 384), (16, 1024), (16, 1536)])
+                                  (8, 1536), (8, 2048), (16, 384), (16, 1024), (16, 1536), (4, 768), (2, 320)])
 def test_sweep_tp(tp, M, full_layer):
-    # rank 5's shard; M = 320 ... 1536 run the narrow gate_up plans (128 x 256 tiles split
+    # rank 5's shard (the last rank at TP4 / TP2); M = 320 ... 1536 run the narrow gate_up plans (128 x 256 tiles split
     # 3-12 ways, or 8-wave 128 x 64 tiles) and the unsplit short-K down tiles (128 x 64 or
     # 128 x 128), 320 and 1000 with a ragged token tile
     wgu, wd, wgu64, wd64 = full_layer
-    g_r, d_r = oracle.rank_shard(wgu64, wd64, tp, 5)
+    r = min(5, tp - 1)
+    g_r, d_r = oracle.rank_shard(wgu64, wd64, tp, r)
     x = synth.activations(M, H, config=5, copy=10000 * tp + M)
-    wgu_r, wd_r = slice_on_gpu(wgu.to(DEV), wd.to(DEV), tp, 5)
+    wgu_r, wd_r = slice_on_gpu(wgu.to(DEV), wd.to(DEV), tp, r)
     out = run_forward(x.to(DEV), wgu_r, wd_r, partial=True)
     ref = oracle.swiglu_mlp(f64(x), g_r, d_r)
     assert_rms_close(out, ref, BF16_TOL, f"sweep tp{tp} M={M}")
