@@ -19,7 +19,11 @@ extern "C" {
 /* stage: 0 = gate_up, 1 = down, 2 = the plain projection of smlp_latent.h (kind 3
  * only).  kind in {0,2,3}; nb in {0,...,4}; waves in {0,4,8}; u in {0,...,8};
  * 0 <= ksplit <= 1024.  Returns SMLP_OK or SMLP_ERR_ARG.  A pinned combination that is
- * not a compiled kernel makes later plans fail with SMLP_ERR_ARG. */
+ * not a compiled kernel makes later plans fail with SMLP_ERR_ARG.  With nb, waves or u
+ * pinned, a K-split stage is reduced by a separate finalize launch instead of in its own
+ * launch (a pinned ksplit alone keeps the in-launch reduction): a sweep of pinned
+ * streaming shapes with K splits once ended in an unexplained GPU memory fault, and the
+ * in-launch form is tested only with the planner's own shapes. */
 int shared_mlp_tune_skinny(int stage, int kind, int nb, int waves, int u, int ksplit);
 
 /* The LDS-tiled (large-M) stages (stage 2: the plain projection, planned like down):
