@@ -629,7 +629,7 @@ int make_plan(int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32, smlp
     p->path = SMLP_PATH_FP32;
     p->h_dtype = SMLP_FP32;
     p->h_bytes = round_up((size_t)(M * I) * 4, 256);
-    p->kernels = 2;
+    p->kernels = g_fuse.load() != 2 && smlp::fp32_small_layer(M, H, I) ? 1 : 2;
   } else if (M < g_threshold.load() && M <= kSmallMaxM) {
     p->path = SMLP_PATH_SMALL_M;
     // h as one bf16 plane (rounded once, as the serving stack stores it) when the down
@@ -857,6 +857,10 @@ int run(Stage stage, const void* x, const void* wgu, const void* wd, void* out, 
       return hip_status(smlp::launch_decode_layer(p, x, wgu, wd, out, ws, slot, g_fuse_limit.load(), stream),
                         "decode layer launch");
   }
+  if (stage == kBoth && g_fuse.load() != 2 && p.path == SMLP_PATH_FP32 && smlp::fp32_small_layer(p.M, p.H, p.I))
+    return hip_status(smlp::launch_fp32_layer(p, (const float*)x, (const float*)wgu, (const float*)wd,
+                                              (float*)out, stream),
+                      "fp32 layer launch");
   if (stage != kDown) {
     switch (p.path) {
       case SMLP_PATH_FP32:

@@ -44,6 +44,47 @@ __global__ __launch_bounds__(256) void fp32_down_kernel(const float* __restrict_
   }
 }
 
+// The whole fp32 layer in one workgroup when h fits in LDS (the small equivalence-test
+// shapes, where two dependent launches cost more than the arithmetic): the same
+// per-element loops as the two kernels above (fmaf over k, then over i, in order), so
+// the same bits, with h held in LDS between the stages.
+__global__ __launch_bounds__(256) void fp32_layer_small_kernel(const float* __restrict__ x,
+                                                               const float* __restrict__ w,
+                                                               const float* __restrict__ wd, int M, int H,
+                                                               int I, int up_off, int ldw,
+                                                               float* __restrict__ out) {
+  __shared__ float h[kFp32SmallH];
+  for (int e = threadIdx.x; e < M * I; e += blockDim.x) {
+    const int m = e / I, i = e % I;
+    const float* xr = x + (size_t)m * H;
+    const float* gr = w + (size_t)i * H;
+    const float* ur = w + ((size_t)up_off + i) * H;
+    float g = 0.f, u = 0.f;
+    for (int k = 0; k < H; ++k) {
+      g = fmaf(xr[k], gr[k], g);
+      u = fmaf(xr[k], ur[k], u);
+    }
+    h[e] = silu_mul(g, u);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < M * H; e += blockDim.x) {
+    const int m = e / H, n = e % H;
+    const float* hr = h + m * I;
+    const float* wr = wd + (size_t)n * ldw;
+    float acc = 0.f;
+    for (int i = 0; i < I; ++i) acc = fmaf(hr[i], wr[i], acc);
+    out[e] = acc;
+  }
+}
+
+int launch_fp32_layer(const Plan& p, const float* x, const float* w_gate_up, const float* w_down, float* out,
+                      hipStream_t s) {
+  if (!fp32_small_layer(p.M, p.H, p.I)) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(fp32_layer_small_kernel, dim3(1), dim3(256), 0, s, x, w_gate_up, w_down, (int)p.M,
+                     (int)p.H, (int)p.I, (int)p.up_off, (int)p.ldwd, out);
+  return (int)hipGetLastError();
+}
+
 static int grid_for(size_t total) {
   size_t b = (total + 255) / 256;
   return (int)(b > 8192 ? 8192 : (b < 1 ? 1 : b));

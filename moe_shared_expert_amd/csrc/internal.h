@@ -115,6 +115,14 @@ int noalloc_scratch(void** ptr);
 int launch_fp32_gate_up(const Plan& p, const float* x, const float* w_gate_up, void* ws,
                         hipStream_t s);
 int launch_fp32_down(const Plan& p, const float* w_down, float* out, void* ws, hipStream_t s);
+// Both fp32 stages in one single-workgroup launch, h in LDS, where M * I <= kFp32SmallH and
+// M * H * I <= 2^20 (fp32_small_layer); the same bits as the two launches above.
+constexpr int kFp32SmallH = 4096;
+inline bool fp32_small_layer(int64_t M, int64_t H, int64_t I) {
+  return M * I <= kFp32SmallH && M * H * I <= ((int64_t)1 << 20);
+}
+int launch_fp32_layer(const Plan& p, const float* x, const float* w_gate_up, const float* w_down, float* out,
+                      hipStream_t s);
 int launch_slice_rank(const void* wgu, const void* wd, void* wgu_r, void* wd_r, int64_t H,
                       int64_t I, int tp, int rank, int elem_bytes, hipStream_t s);
 int launch_rms_rescale(const float* in, uint16_t* out, int64_t M, int64_t H, hipStream_t s);

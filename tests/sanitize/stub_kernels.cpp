@@ -28,6 +28,9 @@ int launch_gemm_gate_up(const Plan&, const void*, const void*, void*, hipStream_
 int launch_gemm_down(const Plan&, const void*, void*, void*, hipStream_t) { return (int)hipErrorNotReady; }
 int launch_fp32_gate_up(const Plan&, const float*, const float*, void*, hipStream_t) { return (int)hipErrorNotReady; }
 int launch_fp32_down(const Plan&, const float*, float*, void*, hipStream_t) { return (int)hipErrorNotReady; }
+int launch_fp32_layer(const Plan&, const float*, const float*, const float*, float*, hipStream_t) {
+  return (int)hipErrorNotReady;
+}
 int launch_slice_rank(const void*, const void*, void*, void*, int64_t, int64_t, int, int, int, hipStream_t) {
   return (int)hipErrorNotReady;
 }

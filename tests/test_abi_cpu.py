@@ -401,7 +401,12 @@ def test_layer_fusion_plan_and_hook(L):
         binding.shared_mlp_tune_h_planes(2)
         assert binding.shared_mlp_plan(16, H, I)["kernels"] == 2
         binding.shared_mlp_tune_h_planes(0)
+        assert binding.shared_mlp_plan(12, 16, 12, FP32)["kernels"] == 1      # one-workgroup fp32 layer
+        assert binding.shared_mlp_plan(40, 64, 100, FP32)["kernels"] == 1
+        assert binding.shared_mlp_plan(41, 64, 100, FP32)["kernels"] == 2     # h past 4096 floats
+        assert binding.shared_mlp_plan(16, 4096, 64, FP32)["kernels"] == 2    # past 2^20 multiply-adds
         binding.shared_mlp_tune_layer_fusion(2, 0)
+        assert binding.shared_mlp_plan(12, 16, 12, FP32)["kernels"] == 2
         assert binding.shared_mlp_plan(16, H, I)["kernels"] == 2
         binding.shared_mlp_tune_layer_fusion(1, 1000)
         assert binding.shared_mlp_plan(16, H, I)["kernels"] == 1

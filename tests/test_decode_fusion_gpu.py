@@ -11,14 +11,17 @@
   the last-arriving slice of each column sums the partials and applies the epilogue in
   the same launch; the same bits as the separate finalize launch.
 
-shared_mlp_tune_layer_fusion switches both off (mode 2) for the comparisons.
+- Small fp32 layers (M * I <= 4096, M * H * I <= 2^20): both stages in one single-workgroup
+  launch with h in LDS; the same bits as the two fp32 launches.
+
+shared_mlp_tune_layer_fusion switches these off (mode 2) for the comparisons.
 """
 import pytest
 import torch
 
 import oracle
 import synth
-from parity_util import BF16_TOL, DEV, H, I, assert_rms_close, f64, workspace_for
+from parity_util import BF16_TOL, DEV, FP32_TOL, H, I, assert_rms_close, f64, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -211,3 +214,39 @@ def test_ksplit_projection_reduced_in_launch_matches_finalize(N):
     for rep in range(2):
         one, sep = both_forms(proj)
         assert torch.isfinite(one.float()).all() and torch.equal(one, sep), f"N={N} rep {rep}"
+
+
+# --------------------------------------- small fp32 layers in one single-workgroup launch
+@pytest.mark.parametrize("M,Hh,Ii", [(12, 16, 12), (40, 64, 100), (7, 136, 24), (1, 8, 8)])
+def test_fp32_one_launch_matches_two_launches_bit_for_bit(M, Hh, Ii):
+    g = torch.Generator().manual_seed(M * 1000 + Hh + Ii)
+    x = torch.randn(M, Hh, generator=g)
+    wgu = torch.randn(2 * Ii, Hh, generator=g)
+    wd = torch.randn(Hh, Ii, generator=g)
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), wd.to(DEV)
+
+    def fwd():
+        out = torch.full((M, Hh), float("nan"), dtype=torch.float32, device=DEV)
+        binding.shared_mlp_forward(xd, gd, dd, out, workspace=workspace_for(M, Hh, Ii, binding.SMLP_FP32))
+        return out
+    assert binding.shared_mlp_plan(M, Hh, Ii, binding.SMLP_FP32)["kernels"] == 1
+    one, two = both_forms(fwd)
+    assert torch.equal(one, two), f"M={M} H={Hh} I={Ii}: one-launch and two-launch fp32 layers differ"
+    ref = oracle.swiglu_mlp(f64(x), f64(wgu), f64(wd))
+    assert_rms_close(one, ref, FP32_TOL, f"fp32 one launch M={M} H={Hh} I={Ii}")
+
+
+def test_fp32_one_launch_rank_views():
+    # ranks in place (up rows I further on, w_down row stride I) on the single-workgroup form
+    x, gate, up, down, tp, _ = synth.tiny_fp32_case()
+    wgu = synth.merged_gate_up(gate, up)
+    xd, gd, dd = x.to(DEV), wgu.to(DEV), down.to(DEV)
+    for r in range(tp):
+        def fwd():
+            out = torch.full(tuple(x.shape[:1]) + (down.shape[0],), float("nan"), dtype=torch.float32, device=DEV)
+            binding.shared_mlp_forward_rank(xd, gd, dd, out, tp, r)
+            return out
+        one, two = both_forms(fwd)
+        assert torch.equal(one, two), f"rank {r}"
+        ref = oracle.rank_partial(f64(x), f64(wgu), f64(down), tp, r)
+        assert_rms_close(one, ref, FP32_TOL, f"fp32 one launch rank {r}")
