@@ -731,7 +731,8 @@ def sweep(dev, steps):
     cycled, hipGraph replays; M <= 512: `steps` calls per trial, larger M at most 40),
     then the replicated-vs-sharded crossover that the measured curves give under a model
     of the two collectives (include/smlp_layout.h)."""
-    Ms = [1, 8, 32, 128, 512, 2048, 8192]
+    # 256 and 1024 bracket the replicated/sharded crossover more closely than 128 / 512 / 2048
+    Ms = [1, 8, 32, 128, 256, 512, 1024, 2048, 8192]
     curves = {}
     points = []
     stream = torch.cuda.Stream(dev)
