@@ -93,7 +93,8 @@ typedef struct {
   int gate_up_blocks;     /* workgroups of the gate_up stage's main kernel                */
   int down_blocks;        /* workgroups of the down stage's main kernel                   */
   int kernels;            /* kernel launches per forward call (1 for the one-launch      */
-                          /* decode layer; 2 there on a stream past the 16th per device)  */
+                          /* decode layer, 2 there on a stream past the 16th per device;  */
+                          /* 1 for a small fp32 layer, M*I <= 4096 and M*H*I <= 2^20)      */
 } smlp_plan;
 
 /* Plan of shared_mlp_forward for these sizes.  Host-only; no HIP call. */
@@ -119,7 +120,8 @@ int shared_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int dtype, size_
  * two-launch form).  Calls on one stream, and on different streams, may run as usual;
  * two replays of one captured graph must not run at the same time (they share the
  * capturing stream's counters).  If a down workgroup ever gives up waiting, its output
- * rows are NaN.
+ * rows are NaN.  A small fp32 layer (M * I <= 4096, M * H * I <= 2^20) runs both stages
+ * in one single-workgroup launch with h in LDS; the workspace is still required.
  */
 int shared_mlp_forward(const void* x, const void* w_gate_up, const void* w_down, void* out,
                        int64_t M, int64_t H, int64_t I, int dtype, int partial_fp32,
